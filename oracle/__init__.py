@@ -1,0 +1,12 @@
+"""fp64 CPU oracle for gated retention (test infrastructure only).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. It shares no code with the HIP library, and the library
+never imports it.
+"""
+from .oracle import (  # noqa: F401
+    build_oracle,
+    oracle_decode_f64,
+    oracle_max_threads,
+    oracle_prefill_f64,
+)

@@ -1,0 +1,56 @@
+"""Checks of the shared seeded input generator (no retention arithmetic here)."""
+import numpy as np
+import torch
+
+from workloads import (CONFIGS, LN_SHARP_GAMMA, bf16_bits_to_f32, f32_to_bf16_bits,
+                       make_decode_inputs, make_prefill_inputs)
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 3,
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 65504.0, 1e-30],
+                                 np.float32)])
+    ours = f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    back = bf16_bits_to_f32(ours)
+    np.testing.assert_array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_prefill_inputs_are_deterministic_and_per_head():
+    a = make_prefill_inputs(2, N=256, H=3)
+    b = make_prefill_inputs(2, N=256, H=3)
+    for key in ("q", "k", "v", "log_gamma"):
+        np.testing.assert_array_equal(a[key], b[key])
+    # one stream per head: drawing a subset reproduces the same head
+    c = make_prefill_inputs(2, N=256, H=3, heads=[1])
+    np.testing.assert_array_equal(c["q"][0, 1], a["q"][0, 1])
+    assert not c["q"][0, 0].any()
+
+
+def test_prefill_value_statistics():
+    d = make_prefill_inputs(3, N=65536, H=2)
+    lg = d["log_gamma"]
+    assert lg.dtype == np.float32 and np.all(lg <= 0)
+    sharp = lg == LN_SHARP_GAMMA
+    assert 0.007 < sharp.mean() < 0.013
+    rest = lg[~sharp]
+    assert abs(rest.mean() - (-0.0504)) < 0.002
+    q = bf16_bits_to_f32(d["q"]).astype(np.float64)
+    v = bf16_bits_to_f32(d["v"]).astype(np.float64)
+    assert abs(q.var() * 128 - 1.0) < 0.02
+    assert abs(v.var() - 1.0) < 0.02
+
+
+def test_config_table():
+    assert CONFIGS[1]["dtype"] == "f32" and CONFIGS[1]["chunks"] == (64,)
+    assert CONFIGS[3]["N"] == 524288 and CONFIGS[4]["N"] == 1048576
+    assert CONFIGS[4]["s0_std"] == 0.1 and CONFIGS[3]["sharp_frac"] == 0.01
+
+
+def test_decode_inputs_shapes():
+    d = make_decode_inputs(5, B=2, H=3, steps=4)
+    assert d["state"].shape == (2, 3, 128, 128)
+    assert d["q"].shape == (4, 2, 3, 128) and d["q"].dtype == np.uint16
+    assert abs(d["state"].std() - 0.1) < 0.005
