@@ -1,0 +1,262 @@
+"""Benchmark: gated-retention prefill (512K positions, 24 heads x 128) and
+batched decode on one MI355X, with roofline and CPU-oracle baselines.
+
+One bench step = one chunkwise prefill of the long-prompt workload
+(B=1, H=24, N=524288, dk=dv=128, bf16 inputs, fp32 log-gates, 1% of positions
+forced to gamma=0.1). The decode workload (256 sequences x 24 heads, fp32
+state 384 MiB, 1000 consecutive steps with fresh tokens) is timed after it and
+reported in the same JSON line. Inputs are seeded synthetic data already
+resident in HBM when timing starts.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk C]
+                       [--skip-cpu] [--only prefill|decode] [--sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix
+METRIC = "gRet prefill tokens/s @N=512K, 24h×128; decode steps/s; % of roofline"
+DEFAULT_CHUNK = 64
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def prefill_algorithmic(B, H, N, dk, dv, chunk, state_in):
+    """Bytes that must cross HBM (inputs read once, outputs written once) and
+    the flops of the chunkwise form at this chunk size (causal tiles only)."""
+    esz = 2
+    per_tok = (2 * dk + dv) * esz + dv * esz + 4
+    state = B * H * dk * dv * 4 * (2 if state_in else 1)
+    nbytes = B * H * N * per_tok + state
+    flops = B * H * N * ((chunk + 1) * (dk + dv) + 4 * dk * dv)
+    return nbytes, flops
+
+
+def decode_algorithmic(B, H, dk, dv):
+    nbytes = 2 * B * H * dk * dv * 4 + B * H * (2 * dk + 2 * dv) * 2 + 4 * B * H
+    flops = 5 * B * H * dk * dv
+    return nbytes, flops
+
+
+def cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def to_dev(a, dev):
+    import torch
+
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def time_prefill(gret, d, chunk, steps, warmup, dev):
+    import torch
+
+    q, k, v = to_dev(d["q"], dev), to_dev(d["k"], dev), to_dev(d["v"], dev)
+    lg = to_dev(d["log_gamma"], dev)
+    si = None if d.get("s0") is None else to_dev(d["s0"], dev)
+    B, H, N, dk = d["q"].shape
+    dv = d["v"].shape[3]
+    out = torch.empty((B, H, N, dv), dtype=torch.bfloat16, device=dev)
+    so = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    need = gret.gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, 1)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        gret.gret_prefill(q, k, v, lg, si, chunk=chunk, out=out, state_out=so, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        gret.gret_prefill(q, k, v, lg, si, chunk=chunk, out=out, state_out=so, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del q, k, v, lg, out, so, ws
+    torch.cuda.empty_cache()
+    return ms
+
+
+def bench_decode(gret, dev, steps_total, reps, warmup_reps):
+    import torch
+
+    from workloads import make_decode_inputs
+
+    t0 = time.time()
+    d = make_decode_inputs(5, steps=steps_total)
+    log("decode inputs generated in %.1f s" % (time.time() - t0))
+    B, H, dk, dv = d["B"], d["H"], d["dk"], d["dv"]
+    state = to_dev(d["state"], dev)
+    q, k, v, lg = (to_dev(d[x], dev) for x in ("q", "k", "v", "log_gamma"))
+    out = torch.empty((B, H, dv), dtype=torch.bfloat16, device=dev)
+
+    def run():
+        for t in range(steps_total):
+            gret.gret_decode_step(q[t], k[t], v[t], lg[t], state, out=out)
+
+    for _ in range(warmup_reps):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_per_step = e0.elapsed_time(e1) * 1000.0 / (reps * steps_total)
+    nbytes, flops = decode_algorithmic(B, H, dk, dv)
+    achieved = nbytes / (us_per_step * 1e-6) / 1e9
+    res = {
+        "workload": "decode_b256h24_d128_1000steps",
+        "steps_per_s": 1e6 / us_per_step,
+        "us_per_step": us_per_step,
+        "timed_steps": reps * steps_total,
+        "roofline": {"kernel": "decode_step_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes},
+    }
+    del state, q, k, v, lg, out
+    torch.cuda.empty_cache()
+    return res, d
+
+
+def cpu_prefill_baseline(d, n_sample):
+    import oracle
+
+    threads = cpu_threads()
+    sl = {x: np.ascontiguousarray(d[x][:, :, :n_sample]) for x in ("q", "k", "v", "log_gamma")}
+    t0 = time.time()
+    oracle.oracle_prefill_f64(sl["q"], sl["k"], sl["v"], sl["log_gamma"], want_out=False,
+                              nthreads=threads)
+    dt = time.time() - t0
+    B, H = d["q"].shape[:2]
+    return {"value": B * n_sample / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d positions of all %d heads of the 512K workload (fp64 recurrence, "
+                      "%.1f s)" % (n_sample, B * H, dt)}
+
+
+def cpu_decode_baseline(d, n_steps):
+    import oracle
+
+    threads = cpu_threads()
+    s = d["state"].astype(np.float64)
+    t0 = time.time()
+    for t in range(n_steps):
+        oracle.oracle_decode_f64(d["q"][t], d["k"][t], d["v"][t], d["log_gamma"][t], s,
+                                 nthreads=threads)
+    dt = time.time() - t0
+    return {"value": n_steps / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d of the 1000 steps, all 256x24 heads (fp64, %.1f s)" % (n_steps, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=DEFAULT_CHUNK)
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--decode-reps", type=int, default=1)
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time chunk 64/128/256 on the 32K and 512K workloads (stderr)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads and sequences shard across GPUs without communication; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import yoco_gated_retention_amd as gret
+    from workloads import CONFIGS, make_prefill_inputs
+
+    gret.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic (seeded; value distributions of the pages' gRet gate)"}
+
+    d3 = None
+    if args.only in (None, "prefill"):
+        cfg = CONFIGS[3]
+        t0 = time.time()
+        d3 = make_prefill_inputs(3)
+        log("prefill inputs generated in %.1f s" % (time.time() - t0))
+        ms = time_prefill(gret, d3, args.chunk, args.steps, args.warmup, dev)
+        B, H, N, dk, dv = 1, cfg["H"], cfg["N"], cfg["dk"], cfg["dv"]
+        nbytes, flops = prefill_algorithmic(B, H, N, dk, dv, args.chunk, False)
+        achieved = nbytes / (ms * 1e-3) / 1e9
+        result.update({
+            "value": B * N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "config": {"workload": cfg["name"], "B": B, "H": H, "N": N, "dk": dk, "dv": dv,
+                       "chunk": args.chunk, "log_gamma": "fp32", "state": "fp32",
+                       "inputs": "bf16"},
+            "roofline": {"kernel": "gret_prefill (main + combine + prefix launches)",
+                         "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "algorithmic_bytes_per_launch": nbytes,
+                         "mfma_tflops": flops / (ms * 1e-3) / 1e12,
+                         "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        })
+        log("prefill chunk=%d: %.3f ms/step, %.3e tokens/s, %.0f GB/s (%.1f%% of HBM peak)" % (
+            args.chunk, ms, result["value"], achieved, 100 * achieved / HBM_PEAK_GBS))
+        if args.sweep:
+            for cid in (2, 3):
+                dd = d3 if cid == 3 else make_prefill_inputs(2)
+                c = CONFIGS[cid]
+                for ch in (64, 128, 256):
+                    m = time_prefill(gret, dd, ch, max(3, args.steps // 2), 2, dev)
+                    nb, fl = prefill_algorithmic(1, c["H"], c["N"], c["dk"], c["dv"], ch, False)
+                    log(json.dumps({"sweep": c["name"], "chunk": ch, "ms": m,
+                                    "tokens_per_s": c["N"] / (m * 1e-3),
+                                    "hbm_frac": nb / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                    "mfma_frac": fl / (m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}))
+        if not args.skip_cpu:
+            result["cpu_baseline"] = cpu_prefill_baseline(d3, 131072)
+            log("cpu baseline: %s" % json.dumps(result["cpu_baseline"]))
+
+    if args.only in (None, "decode"):
+        dec, dd = bench_decode(gret, dev, CONFIGS[5]["decode_steps"], args.decode_reps, 1)
+        if not args.skip_cpu:
+            dec["cpu_baseline"] = cpu_decode_baseline(dd, 100)
+        result["decode"] = dec
+        log("decode: %.2f us/step, %.0f steps/s, %.0f GB/s (%.1f%%)" % (
+            dec["us_per_step"], dec["steps_per_s"], dec["roofline"]["achieved"],
+            100 * dec["roofline"]["frac"]))
+        if args.only == "decode":
+            result.update({"value": dec["steps_per_s"], "unit": "steps/s",
+                           "ms_per_step": dec["us_per_step"] / 1000.0,
+                           "config": {"workload": dec["workload"]},
+                           "roofline": dec["roofline"]})
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

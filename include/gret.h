@@ -1,0 +1,154 @@
+/*
+ * gret.h -- C ABI of libgret, multi-head gated retention (gRet) on AMD gfx950.
+ *
+ * The method is the Self-Decoder mixer described on the page
+ * "YOCO 完全拆解：Decoder-Decoder 架构如何让 KV Cache 只存一次":
+ *   section "路线二：Multi-Head Gated Retention" -- per head, a dk x dv matrix
+ *     state is scaled by one data-dependent scalar gate per position and
+ *     receives the key/value outer product; the output is the query times the
+ *     updated state:  S_n = g_n S_{n-1} + k_n^T v_n,  o_n = q_n S_n;
+ *   section "Prefill 与 Decode 为什么使用两种计算形态" -- prompts are processed
+ *     in the chunkwise form (decayed causal attention inside a chunk, the
+ *     carried state for everything before it), decode steps in the recurrent
+ *     form; both are the same formula, the chunk size is only a tuning knob;
+ *   section "Prefill 的实现骨架" -- a prompt that is not a multiple of the chunk
+ *     size is masked at its tail, and the state at the end of prefill is kept
+ *     for the decode steps that follow;
+ *   section "单 token Decode 的实现骨架" -- a decode step multiplies the old
+ *     state by the exponential of the gate value and adds the key/value outer
+ *     product, which is why this ABI takes the log of the gate.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers. Every tensor pointer is a device pointer owned by the caller. The
+ *   library never allocates device memory, never frees or retains a pointer
+ *   after the call returns, keeps no global state and is reentrant.
+ * Layouts (contiguous, row-major, head-major as [batch, head, position, dim]):
+ *   prefill  q, k [B,H,N,dk]; v, out [B,H,N,dv]; log_gamma [B,H,N]
+ *   decode   q, k [B,H,dk];   v, out [B,H,dv];   log_gamma [B,H]
+ *   state    [B,H,dk,dv], element [i][j] pairs key dim i with value dim j
+ * Types. q, k, v and out use `dtype` (GRET_DTYPE_BF16 or GRET_DTYPE_F32);
+ *   log_gamma and the state are always fp32. bf16 outputs are rounded to
+ *   nearest-even. The bf16 path computes contractions on bf16 matrix cores
+ *   with fp32 accumulation and an fp32 state carry; the fp32 path computes
+ *   everything in fp32.
+ * Gates. log_gamma holds log(gamma) per position; it must lie in [-inf, 0]
+ *   (gamma in [0, 1], as the page's sigmoid gate always gives). Kernels clamp
+ *   it to [GRET_LOG_GAMMA_FLOOR, 0]; the floor stands in for gamma = 0, whose
+ *   log (-inf) would make the chunkwise form compute -inf - (-inf). NaN or
+ *   positive values give unspecified (but finite-time, in-bounds) results.
+ * Scaling. There is no scale argument: keys are expected to arrive already
+ *   multiplied by dk^(-1/2), as the page's implementation does before the
+ *   update. There is no position argument: gRet has no positional term.
+ * Errors. Arguments are validated synchronously; on any failure the call
+ *   returns a nonzero gret_status_t and launches nothing. On success the work
+ *   is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *   returns GRET_OK without synchronising. A launch failure is reported as
+ *   GRET_ERR_HIP; any HIP error already pending on the calling thread is
+ *   cleared before the launch. No C++ exception crosses this ABI.
+ */
+#ifndef GRET_H
+#define GRET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GRET_DTYPE_F32 = 0,
+    GRET_DTYPE_BF16 = 1
+} gret_dtype_t;
+
+typedef enum {
+    GRET_OK = 0,
+    GRET_ERR_NULL = 1,        /* a required pointer is NULL                   */
+    GRET_ERR_SHAPE = 2,       /* B, H or N < 1, or sizes overflow             */
+    GRET_ERR_UNSUPPORTED = 3, /* dk, dv, chunk or dtype outside the set below */
+    GRET_ERR_ALIAS = 4,       /* out overlaps an input, or states overlap
+                                 without being identical                      */
+    GRET_ERR_HIP = 5,         /* a HIP runtime call or launch failed          */
+    GRET_ERR_WORKSPACE = 6    /* workspace missing, too small or misaligned   */
+} gret_status_t;
+
+/* Log-gate floor used in place of -inf (gamma ~ 1.8e-35). */
+#define GRET_LOG_GAMMA_FLOOR (-80.0f)
+
+/* Supported head sizes: dk, dv in {64, 128} (any pairing).
+   Supported prefill chunk sizes: 64, 128, 256. */
+
+/*
+ * gret_prefill_workspace_bytes -- device scratch that gret_prefill needs.
+ *
+ * Prefill splits each head's sequence into segments that run at the same time
+ * and are chained afterwards (the chunkwise form of section "Prefill 与 Decode
+ * 为什么使用两种计算形态", applied at two levels). The partial states live in a
+ * caller-owned workspace whose size depends only on the arguments below (not
+ * on the device). Writes the size to *bytes (0 when none is needed).
+ * Returns GRET_OK or a validation error (GRET_ERR_NULL if bytes is NULL).
+ */
+int gret_prefill_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                                 int64_t chunk, int dtype, size_t* bytes);
+
+/*
+ * gret_prefill -- chunkwise gated retention over a whole prompt.
+ *
+ * For each (b,h): starting from state_in[b,h] (zero when state_in is NULL),
+ * computes out[b,h,n,:] = q_n S_n for n = 0..N-1 with
+ * S_n = exp(log_gamma[b,h,n]) S_{n-1} + k_n^T v_n, and writes S_{N-1} to
+ * state_out[b,h] unless state_out is NULL (sections "路线二：Multi-Head Gated
+ * Retention", "Prefill 与 Decode 为什么使用两种计算形态", "Prefill 的实现骨架").
+ *
+ *   q, k, v, log_gamma  inputs (layouts above), required
+ *   state_in            fp32 [B,H,dk,dv] or NULL (zero initial state)
+ *   out                 output [B,H,N,dv] in dtype, required; must not overlap
+ *                       any input, state_out or the workspace
+ *   state_out           fp32 [B,H,dk,dv] or NULL; may be identical to state_in
+ *                       (in place); any other overlap is GRET_ERR_ALIAS
+ *   B, H, N             >= 1; N need not be a multiple of chunk (the tail chunk
+ *                       is masked and state_out is exactly S_{N-1})
+ *   dk, dv              64 or 128
+ *   chunk               64, 128 or 256 -- the chunk length of the chunkwise form
+ *   dtype               gret_dtype_t of q, k, v, out
+ *   workspace           device scratch of at least
+ *                       gret_prefill_workspace_bytes(...) bytes, 256-byte
+ *                       aligned; may be NULL when that size is 0. Its contents
+ *                       on entry do not matter; calls that share a workspace
+ *                       must be ordered on one stream.
+ *   stream              hipStream_t to enqueue on (NULL = null stream)
+ */
+int gret_prefill(const void* q, const void* k, const void* v, const float* log_gamma,
+                 const float* state_in, void* out, float* state_out, int64_t B, int64_t H,
+                 int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/*
+ * gret_decode_step -- one recurrent step for B*H independent heads.
+ *
+ * state_out[b,h] = exp(log_gamma[b,h]) state_in[b,h] + k[b,h]^T v[b,h] and
+ * out[b,h,:] = q[b,h] state_out[b,h] (the output reads the updated state;
+ * section "单 token Decode 的实现骨架").
+ *
+ *   q, k [B,H,dk], v [B,H,dv] in dtype; log_gamma [B,H] fp32 -- required
+ *   state_in   fp32 [B,H,dk,dv] or NULL (zero state)
+ *   state_out  fp32 [B,H,dk,dv], required; may be identical to state_in (the
+ *              usual in-place update); any other overlap is GRET_ERR_ALIAS
+ *   out        [B,H,dv] in dtype, required; must not overlap any other buffer
+ *   dk, dv     64 or 128;  B, H >= 1
+ * The state streams through HBM once per step (read + write), so this is the
+ * bandwidth-bound half of the method.
+ */
+int gret_decode_step(const void* q, const void* k, const void* v, const float* log_gamma,
+                     const float* state_in, void* out, float* state_out, int64_t B, int64_t H,
+                     int64_t dk, int64_t dv, int dtype, void* stream);
+
+/* Static, human-readable text for a gret_status_t value (never NULL). */
+const char* gret_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRET_H */

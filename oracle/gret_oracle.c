@@ -8,7 +8,8 @@
  *
  * What it computes (page "YOCO 完全拆解：Decoder-Decoder 架构如何让 KV Cache 只存一次",
  * section "路线二：Multi-Head Gated Retention", the state/output recurrence, and
- * section "单 token Decode 的实现骨架", the decode update exp(gate)*state + outer(k, v)):
+ * section "单 token Decode 的实现骨架", where a decode step scales the old state
+ * by the exponential of the gate value and adds the key/value outer product):
  *
  *   for every (batch b, head h) independently, with S a dk x dv matrix:
  *     S <- state_in[b,h]  (zero when no initial state is given)

@@ -1,0 +1,129 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+symbol include/gret.h declares, and rejects bad arguments before touching the
+HIP runtime (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import yoco_gated_retention_amd as gret
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gret.h")
+
+OK, NULL, SHAPE, UNSUP, ALIAS, HIP, WORKSPACE = range(7)
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gret.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gret_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"gret_prefill", "gret_decode_step", "gret_prefill_workspace_bytes",
+            "gret_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert gret.gret_status_string(s).startswith(
+            ["GRET_OK", "GRET_ERR_NULL", "GRET_ERR_SHAPE", "GRET_ERR_UNSUPPORTED",
+             "GRET_ERR_ALIAS", "GRET_ERR_HIP", "GRET_ERR_WORKSPACE"][s])
+    assert gret.gret_status_string(99) == "unknown gret status"
+
+
+def ws_bytes(lib, B, H, N, dk, dv, chunk, dtype):
+    n = ctypes.c_size_t(12345)
+    st = lib.gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, dtype, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_query(lib):
+    assert ws_bytes(lib, 1, 2, 512, 64, 64, 64, F32) == (OK, 0)
+    st, n = ws_bytes(lib, 1, 24, 524288, 128, 128, 64, BF16)
+    assert st == OK and n % 256 == 0 and 0 < n < 256 << 20
+    assert ws_bytes(lib, 1, 2, 512, 96, 64, 64, BF16)[0] == UNSUP
+    assert ws_bytes(lib, 1, 2, 512, 64, 64, 32, BF16)[0] == UNSUP
+    assert ws_bytes(lib, 0, 2, 512, 64, 64, 64, BF16)[0] == SHAPE
+    assert ws_bytes(lib, 1, 2, 512, 64, 64, 64, 7)[0] == UNSUP
+    assert lib.gret_prefill_workspace_bytes(1, 1, 1, 64, 64, 64, 1, None) == NULL
+
+
+# Fake, well-aligned device addresses: validation must reject every call below
+# before any HIP call, so nothing is ever dereferenced.
+BASE = 1 << 40
+MB = 1 << 20
+
+
+def P(i):
+    return ctypes.c_void_p(BASE + i * 256 * MB)
+
+
+def prefill(lib, q=P(0), k=P(1), v=P(2), lg=P(3), si=None, out=P(4), so=P(5), B=1, H=2, N=512,
+            dk=64, dv=64, chunk=64, dtype=BF16, ws=P(6), wsb=1 << 30):
+    return lib.gret_prefill(q, k, v, lg, si, out, so, B, H, N, dk, dv, chunk, dtype, ws, wsb, None)
+
+
+def decode(lib, q=P(0), k=P(1), v=P(2), lg=P(3), si=P(5), out=P(4), so=P(5), B=2, H=3, dk=64,
+           dv=64, dtype=BF16):
+    return lib.gret_decode_step(q, k, v, lg, si, out, so, B, H, dk, dv, dtype, None)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, q=None) == NULL
+    assert prefill(lib, lg=None) == NULL
+    assert prefill(lib, out=None) == NULL
+    assert prefill(lib, N=0) == SHAPE
+    assert prefill(lib, B=-1) == SHAPE
+    assert prefill(lib, B=1 << 40, H=1 << 20) == SHAPE
+    assert prefill(lib, dk=32) == UNSUP
+    assert prefill(lib, dv=256) == UNSUP
+    assert prefill(lib, chunk=100) == UNSUP
+    assert prefill(lib, dtype=3) == UNSUP
+    assert prefill(lib, q=ctypes.c_void_p(BASE + 8)) == UNSUP  # not 16-byte aligned
+    assert prefill(lib, ws=None) == WORKSPACE
+    assert prefill(lib, wsb=16) == WORKSPACE
+    assert prefill(lib, ws=ctypes.c_void_p(BASE + 6 * 256 * MB + 16)) == WORKSPACE
+
+
+def test_prefill_aliasing(lib):
+    # out on top of q
+    assert prefill(lib, out=P(0)) == ALIAS
+    # out overlapping the tail of v (v is 1*2*512*64*2 bytes = 128 KiB)
+    assert prefill(lib, out=ctypes.c_void_p(BASE + 2 * 256 * MB + 64 * 1024)) == ALIAS
+    # states partially overlapping
+    assert prefill(lib, si=P(5), so=ctypes.c_void_p(BASE + 5 * 256 * MB + 4096)) == ALIAS
+    # state_out on top of k
+    assert prefill(lib, so=P(1)) == ALIAS
+    # workspace on top of state_in
+    assert prefill(lib, si=P(7), ws=P(7)) == ALIAS
+
+
+def test_decode_validation(lib):
+    assert decode(lib, so=None) == NULL
+    assert decode(lib, v=None) == NULL
+    assert decode(lib, H=0) == SHAPE
+    assert decode(lib, dk=100) == UNSUP
+    assert decode(lib, dtype=2) == UNSUP
+    assert decode(lib, out=P(5)) == ALIAS           # out on the state
+    assert decode(lib, out=P(2)) == ALIAS           # out on v
+    assert decode(lib, so=ctypes.c_void_p(BASE + 5 * 256 * MB + 1024)) == ALIAS  # partial
+    assert decode(lib, so=P(0)) == ALIAS            # state_out on q
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(gret, "_lib", None)
+    monkeypatch.setattr(gret, "LIB_PATH", "/nonexistent/libgret.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        gret.load_library()

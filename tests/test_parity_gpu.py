@@ -1,0 +1,314 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: eps = max|x - ref| / max|ref| <= 1e-2 for bf16 inputs with fp32
+accumulation and <= 1e-4 on the fp32 path, for outputs and final states; the
+decode check holds per step. Inputs come from the shared seeded generator,
+never from the GPU.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import as_f64, eps, stats_eps, to_dev, to_host
+from workloads import CONFIGS, make_decode_inputs, make_prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 1e-2
+TOL_F32 = 1e-4
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def gret():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import yoco_gated_retention_amd as g
+
+    g.load_library()
+    oracle.build_oracle(force=False)
+    return g
+
+
+def gpu_prefill(gret, d, chunk, s0=None, state_out=True):
+    q, k, v = to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"])
+    lg = to_dev(d["log_gamma"])
+    si = None if s0 is None else to_dev(s0)
+    out, st = gret.gret_prefill(q, k, v, lg, si, chunk=chunk)
+    torch.cuda.synchronize()
+    return to_host(out), to_host(st)
+
+
+def check_prefill(gret, d, chunk, tol, s0=None, label=""):
+    say("prefill %s B=%d H=%d N=%d dk=%d dv=%d chunk=%d" % (
+        label, d["q"].shape[0], d["q"].shape[1], d["q"].shape[2], d["q"].shape[3],
+        d["v"].shape[3], chunk))
+    out, st = gpu_prefill(gret, d, chunk, s0)
+    o_ref, s_ref, _ = oracle.oracle_prefill_f64(d["q"], d["k"], d["v"], d["log_gamma"], s0)
+    e_o, e_s = eps(out, o_ref), eps(st, s_ref)
+    say("   eps_out=%.3e eps_state=%.3e" % (e_o, e_s))
+    assert e_o <= tol and e_s <= tol, (e_o, e_s)
+    return out, st, o_ref, s_ref
+
+
+def small_inputs(B, H, N, dk, dv, dtype="bf16", seed=5, s0=True, lg_mode="gate"):
+    rng = np.random.default_rng(seed)
+    from workloads import f32_to_bf16_bits
+
+    def st(x):
+        return f32_to_bf16_bits(x) if dtype == "bf16" else x.astype(np.float32)
+
+    q = st(rng.standard_normal((B, H, N, dk)).astype(np.float32) / np.sqrt(dk))
+    k = st(rng.standard_normal((B, H, N, dk)).astype(np.float32) / np.sqrt(dk))
+    v = st(rng.standard_normal((B, H, N, dv)).astype(np.float32))
+    if lg_mode == "gate":
+        u = rng.standard_normal((B, H, N))
+        lg = (-np.logaddexp(0.0, -u) / 16.0).astype(np.float32)
+    elif lg_mode == "one":
+        lg = np.zeros((B, H, N), np.float32)
+    elif lg_mode == "zero":
+        lg = np.full((B, H, N), -np.inf, np.float32)
+    elif lg_mode == "mixed":
+        lg = rng.uniform(-1.0, 0.0, (B, H, N)).astype(np.float32)
+        lg[rng.random((B, H, N)) < 0.05] = -np.inf
+    S0 = (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32) if s0 else None
+    return dict(q=q, k=k, v=v, log_gamma=lg), S0
+
+
+# ---------------------------------------------------------------- fp32 path
+
+def test_cfg1_fp32_prefill_then_16_decode_steps(gret):
+    d = make_prefill_inputs(1)
+    out, st, o_ref, s_ref = check_prefill(gret, d, 64, TOL_F32, label="cfg1")
+    state = to_dev(st)
+    s64 = s_ref.copy()
+    for t in range(CONFIGS[1]["decode_steps"]):
+        o = gret.gret_decode_step(to_dev(d["dec_q"][t]), to_dev(d["dec_k"][t]),
+                                  to_dev(d["dec_v"][t]), to_dev(d["dec_log_gamma"][t]), state)
+        torch.cuda.synchronize()
+        o_r = oracle.oracle_decode_f64(d["dec_q"][t], d["dec_k"][t], d["dec_v"][t],
+                                       d["dec_log_gamma"][t], s64)
+        assert eps(to_host(o), o_r) <= TOL_F32
+    assert eps(to_host(state), s64) <= TOL_F32
+
+
+@pytest.mark.parametrize("dk,dv,chunk", [(64, 128, 128), (128, 64, 256), (128, 128, 64)])
+def test_fp32_dims_and_chunks(gret, dk, dv, chunk):
+    d, S0 = small_inputs(1, 2, 700, dk, dv, dtype="f32", seed=dk + dv + chunk)
+    check_prefill(gret, d, chunk, TOL_F32, S0, label="f32")
+
+
+# ---------------------------------------------------------------- bf16 path
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
+def test_bf16_ragged_multi_tile(gret, chunk, dk, dv):
+    d, S0 = small_inputs(2, 3, 1000, dk, dv, seed=chunk + dk + 3 * dv)
+    check_prefill(gret, d, chunk, TOL_BF16, S0, label="ragged")
+
+
+@pytest.mark.parametrize("N", [1, 2, 17, 63, 64, 65, 129, 255, 257])
+@pytest.mark.parametrize("chunk", [64, 256])
+def test_bf16_short_lengths(gret, N, chunk):
+    d, S0 = small_inputs(1, 2, N, 128, 128, seed=N)
+    check_prefill(gret, d, chunk, TOL_BF16, S0, label="short")
+
+
+def test_bf16_many_heads_one_chunk_each(gret):
+    # every (head, chunk) pair becomes its own workgroup range
+    d, S0 = small_inputs(4, 24, 60, 128, 128, seed=9)
+    check_prefill(gret, d, 64, TOL_BF16, S0, label="many-heads")
+
+
+@pytest.mark.parametrize("chunk", [64, 256])
+def test_bf16_gate_one_long(gret, chunk):
+    # gamma = 1: incoming states never decay, every segment is recomputed
+    d, S0 = small_inputs(1, 2, 16384, 128, 128, seed=21, lg_mode="one")
+    check_prefill(gret, d, chunk, TOL_BF16, S0, label="gate-one")
+
+
+def test_bf16_gate_zero_and_mixed_resets(gret):
+    d, S0 = small_inputs(1, 2, 3000, 128, 128, seed=22, lg_mode="zero")
+    check_prefill(gret, d, 64, TOL_BF16, S0, label="gate-zero")
+    d, S0 = small_inputs(1, 4, 5000, 128, 128, seed=23, lg_mode="mixed")
+    check_prefill(gret, d, 128, TOL_BF16, S0, label="mixed")
+
+
+def test_bf16_split_prefill_then_decode(gret):
+    d, S0 = small_inputs(1, 4, 3000, 128, 128, seed=31)
+    N1 = 1777
+    head = {key: val[:, :, :N1] for key, val in d.items()}
+    tail = {key: val[:, :, N1:] for key, val in d.items()}
+    o1, s1 = gpu_prefill(gret, head, 64, S0)
+    o2, s2 = gpu_prefill(gret, tail, 128, s1)
+    o_ref, s_ref, _ = oracle.oracle_prefill_f64(d["q"], d["k"], d["v"], d["log_gamma"], S0)
+    assert eps(np.concatenate([as_f64(o1), as_f64(o2)], axis=2), o_ref) <= TOL_BF16
+    assert eps(s2, s_ref) <= TOL_BF16
+    # continue with decode steps from the GPU state
+    state = to_dev(s2)
+    s64 = s_ref.copy()
+    dd, _ = small_inputs(1, 4, 8, 128, 128, seed=32, s0=False)
+    for t in range(8):
+        args = [np.ascontiguousarray(dd[key][:, :, t]) for key in ("q", "k", "v", "log_gamma")]
+        o = gret.gret_decode_step(*(to_dev(a) for a in args), state)
+        torch.cuda.synchronize()
+        o_r = oracle.oracle_decode_f64(*args, s64)
+        assert eps(to_host(o), o_r) <= TOL_BF16
+    assert eps(to_host(state), s64) <= TOL_BF16
+
+
+def test_bf16_in_place_state_and_no_state_out(gret):
+    d, S0 = small_inputs(2, 2, 900, 128, 128, seed=41)
+    q, k, v, lg = (to_dev(d[key]) for key in ("q", "k", "v", "log_gamma"))
+    st = to_dev(S0)
+    out, st2 = gret.gret_prefill(q, k, v, lg, st, chunk=64, state_out=st)
+    torch.cuda.synchronize()
+    assert st2.data_ptr() == st.data_ptr()
+    o_ref, s_ref, _ = oracle.oracle_prefill_f64(d["q"], d["k"], d["v"], d["log_gamma"], S0)
+    assert eps(to_host(out), o_ref) <= TOL_BF16
+    assert eps(to_host(st), s_ref) <= TOL_BF16
+    # state_out = NULL at the ABI: outputs only
+    lib = gret.load_library()
+    import ctypes
+    out2 = torch.empty_like(out)
+    need = gret.gret_prefill_workspace_bytes(2, 2, 900, 128, 128, 64, 1)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    st0 = to_dev(S0)
+    rc = lib.gret_prefill(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                          ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(lg.data_ptr()),
+                          ctypes.c_void_p(st0.data_ptr()), ctypes.c_void_p(out2.data_ptr()),
+                          None, 2, 2, 900, 128, 128, 64, 1, ctypes.c_void_p(ws.data_ptr()), need,
+                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert torch.equal(out2, out)
+
+
+def test_bf16_bitwise_deterministic(gret):
+    d, S0 = small_inputs(1, 8, 20000, 128, 128, seed=51)
+    a = gpu_prefill(gret, d, 64, S0)
+    b = gpu_prefill(gret, d, 64, S0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------- full-size workloads (configs)
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_cfg2_full(gret, chunk):
+    d = make_prefill_inputs(2)
+    say("cfg2 chunk=%d" % chunk)
+    out, st = gpu_prefill(gret, d, chunk)
+    _, s_ref, stats = oracle.oracle_prefill_f64(d["q"], d["k"], d["v"], d["log_gamma"],
+                                                want_out=False, compare=out)
+    e_o, e_s = stats_eps(stats), eps(st, s_ref)
+    say("   eps_out=%.3e eps_state=%.3e" % (e_o, e_s))
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+
+
+SAMPLE_HEADS = (0, 11, 23)
+
+
+def _sampled_check(gret, cfg_id, chunk, first_chunk=False):
+    d = make_prefill_inputs(cfg_id)
+    s0 = d["s0"]
+    say("cfg%d N=%d chunk=%d (oracle on heads %s)" % (cfg_id, d["N"], chunk, SAMPLE_HEADS))
+    out, st = gpu_prefill(gret, d, chunk, s0)
+    hs = list(SAMPLE_HEADS)
+
+    def sl(a):
+        return np.ascontiguousarray(a[:, hs])
+
+    _, s_ref, stats = oracle.oracle_prefill_f64(sl(d["q"]), sl(d["k"]), sl(d["v"]),
+                                                sl(d["log_gamma"]),
+                                                None if s0 is None else sl(s0),
+                                                want_out=False, compare=sl(out))
+    e_o, e_s = stats_eps(stats), eps(st[:, hs], s_ref)
+    say("   eps_out=%.3e eps_state=%.3e" % (e_o, e_s))
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+    if first_chunk:
+        # the initial state decays within a few hundred positions; check it alone
+        n = chunk
+        o_ref, _, _ = oracle.oracle_prefill_f64(sl(d["q"][:, :, :n]), sl(d["k"][:, :, :n]),
+                                                sl(d["v"][:, :, :n]), sl(d["log_gamma"][:, :, :n]),
+                                                sl(s0))
+        e_f = eps(out[:, hs, :n], o_ref)
+        say("   first-chunk eps=%.3e" % e_f)
+        assert e_f <= TOL_BF16
+
+
+def test_cfg3_full_sampled_heads(gret):
+    _sampled_check(gret, 3, 64)
+
+
+def test_cfg4_full_sampled_heads(gret):
+    _sampled_check(gret, 4, 64, first_chunk=True)
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (64, 128), (128, 128)])
+def test_decode_small(gret, dtype, dk, dv):
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    d, S0 = small_inputs(3, 5, 6, dk, dv, dtype=dtype, seed=dk * 3 + dv)
+    state = to_dev(S0)
+    s64 = S0.astype(np.float64)
+    for t in range(6):
+        args = [np.ascontiguousarray(d[key][:, :, t]) for key in ("q", "k", "v", "log_gamma")]
+        o = gret.gret_decode_step(*(to_dev(a) for a in args), state)
+        torch.cuda.synchronize()
+        o_r = oracle.oracle_decode_f64(*args, s64)
+        assert eps(to_host(o), o_r) <= tol
+    assert eps(to_host(state), s64) <= tol
+    # zero initial state, separate output state
+    args = [np.ascontiguousarray(d[key][:, :, 0]) for key in ("q", "k", "v", "log_gamma")]
+    so = torch.empty_like(state)
+    o = gret.gret_decode_step(*(to_dev(a) for a in args), None, state_out=so)
+    torch.cuda.synchronize()
+    z = np.zeros_like(s64)
+    o_r = oracle.oracle_decode_f64(*args, z)
+    assert eps(to_host(o), o_r) <= tol and eps(to_host(so), z) <= tol
+
+
+def test_cfg5_decode_1000_steps_sampled(gret):
+    cfg = CONFIGS[5]
+    B, H, steps = cfg["B"], cfg["H"], cfg["decode_steps"]
+    rng = np.random.default_rng(5)
+    heads = sorted(rng.choice(B * H, 48, replace=False).tolist())
+    say("cfg5 decode B=%d H=%d steps=%d, oracle on %d heads" % (B, H, steps, len(heads)))
+    d = make_decode_inputs(5, heads=heads)
+    state = to_dev(d["state"])
+    q, k, v, lg = (to_dev(d[key]) for key in ("q", "k", "v", "log_gamma"))
+    hidx = torch.tensor(heads, device="cuda")
+    outs = []
+    for t in range(steps):
+        o = gret.gret_decode_step(q[t], k[t], v[t], lg[t], state)
+        outs.append(o.view(B * H, -1).index_select(0, hidx))
+    torch.cuda.synchronize()
+    outs = to_host(torch.stack(outs))
+    st = to_host(state).reshape(B * H, 128, 128)[heads]
+    flat = lambda a: a.reshape((a.shape[0], B * H) + a.shape[3:])[:, heads]  # noqa: E731
+    s64 = d["state"].reshape(B * H, 128, 128)[heads].astype(np.float64)
+    qh, kh, vh = flat(d["q"]), flat(d["k"]), flat(d["v"])
+    lh = d["log_gamma"].reshape(steps, B * H)[:, heads]
+    worst = 0.0
+    for t in range(steps):
+        o_r = oracle.oracle_decode_f64(np.ascontiguousarray(qh[t]), np.ascontiguousarray(kh[t]),
+                                       np.ascontiguousarray(vh[t]), np.ascontiguousarray(lh[t]),
+                                       s64)
+        worst = max(worst, eps(outs[t], o_r))
+    e_s = eps(st, s64)
+    say("   worst per-step eps=%.3e final-state eps=%.3e" % (worst, e_s))
+    assert worst <= TOL_BF16 and e_s <= TOL_BF16
+
+
+if __name__ == "__main__":  # pragma: no cover
+    sys.exit(pytest.main([os.path.abspath(__file__), "-x", "-v", "-m", "gpu"]))

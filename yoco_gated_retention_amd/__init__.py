@@ -1,0 +1,178 @@
+"""Python binding of libgret (gated retention on AMD gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/gret.h``. PyTorch supplies the
+device memory and the current HIP stream. There is no CPU fallback; if the
+library is not built, every call raises.
+
+Functions mirror the C ABI names:
+  gret_prefill(q, k, v, log_gamma, state_in=None, chunk=64, out=None,
+               state_out=None, workspace=None) -> (out, state_out)
+  gret_decode_step(q, k, v, log_gamma, state_in, out=None, state_out=None) -> out
+  gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, dtype) -> int
+  gret_status_string(status) -> str
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgret.so")
+
+GRET_DTYPE_F32 = 0
+GRET_DTYPE_BF16 = 1
+GRET_OK = 0
+
+_lock = threading.Lock()
+_lib = None
+
+
+class GretError(RuntimeError):
+    """A libgret call returned a nonzero status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s" % (where, gret_status_string(status)))
+
+
+def load_library():
+    """Load libgret.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgret.so is not built (%s); run __graft_entry__.build() or "
+                               "python -m yoco_gated_retention_amd.build" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        lib.gret_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci,
+                                     vp, sz, vp]
+        lib.gret_prefill.restype = ci
+        lib.gret_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ci, vp]
+        lib.gret_decode_step.restype = ci
+        lib.gret_prefill_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci,
+                                                     ctypes.POINTER(sz)]
+        lib.gret_prefill_workspace_bytes.restype = ci
+        lib.gret_status_string.argtypes = [ci]
+        lib.gret_status_string.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def gret_status_string(status: int) -> str:
+    return load_library().gret_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GRET_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return GRET_DTYPE_F32
+    raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _check_dev(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    n = ctypes.c_size_t(0)
+    st = load_library().gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, code,
+                                                     ctypes.byref(n))
+    if st != GRET_OK:
+        raise GretError(st, "gret_prefill_workspace_bytes")
+    return int(n.value)
+
+
+def gret_prefill(q, k, v, log_gamma, state_in=None, chunk=64, out=None, state_out=None,
+                 workspace=None):
+    """Chunkwise prefill. q, k [B,H,N,dk]; v [B,H,N,dv]; log_gamma [B,H,N] fp32;
+    state_in [B,H,dk,dv] fp32 or None. Returns (out [B,H,N,dv], state_out)."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("log_gamma", log_gamma, torch.float32)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,N,dk] and v [B,H,N,dv]")
+    B, H, N, dk = q.shape
+    dv = v.shape[3]
+    if tuple(log_gamma.shape) != (B, H, N):
+        raise ValueError("log_gamma must be [B,H,N]")
+    if state_in is not None:
+        _check_dev("state_in", state_in, torch.float32)
+        if tuple(state_in.shape) != (B, H, dk, dv):
+            raise ValueError("state_in must be [B,H,dk,dv]")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    else:
+        _check_dev("out", out, q.dtype)
+    if state_out is None:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    else:
+        _check_dev("state_out", state_out, torch.float32)
+    code = _dtype_code(q)
+    need = gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, code)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gret_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(state_in), _ptr(out),
+                          _ptr(state_out), B, H, N, dk, dv, chunk, code, _ptr(workspace), ws_bytes,
+                          _stream())
+    if st != GRET_OK:
+        raise GretError(st, "gret_prefill")
+    return out, state_out
+
+
+def gret_decode_step(q, k, v, log_gamma, state_in, out=None, state_out=None):
+    """One recurrent step. q, k [B,H,dk]; v [B,H,dv]; log_gamma [B,H] fp32;
+    state_in [B,H,dk,dv] fp32 (or None = zero). state_out defaults to state_in
+    (in-place update). Returns out [B,H,dv]."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("log_gamma", log_gamma, torch.float32)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k must be [B,H,dk] and v [B,H,dv]")
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    if tuple(log_gamma.shape) != (B, H):
+        raise ValueError("log_gamma must be [B,H]")
+    if state_in is not None:
+        _check_dev("state_in", state_in, torch.float32)
+    if state_out is None:
+        if state_in is None:
+            raise ValueError("state_out is required when state_in is None")
+        state_out = state_in
+    _check_dev("state_out", state_out, torch.float32)
+    if tuple(state_out.shape) != (B, H, dk, dv):
+        raise ValueError("state must be [B,H,dk,dv]")
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    else:
+        _check_dev("out", out, q.dtype)
+    st = lib.gret_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(state_in),
+                              _ptr(out), _ptr(state_out), B, H, dk, dv, _dtype_code(q), _stream())
+    if st != GRET_OK:
+        raise GretError(st, "gret_decode_step")
+    return out

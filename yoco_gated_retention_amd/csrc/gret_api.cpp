@@ -1,0 +1,221 @@
+// gret_api.cpp -- the C ABI of libgret: argument validation, aliasing rules,
+// prefill planning and dispatch to the kernels. Validation never touches the
+// HIP runtime, so a rejected call has no side effect at all.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/gret.h"
+#include "gret_internal.h"
+
+namespace {
+
+using gret::SegPlan;
+
+constexpr int64_t kMaxElems = int64_t(1) << 50;  // guards size arithmetic
+
+struct Span {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+
+Span span_of(const void* p, int64_t bytes) {
+    Span s;
+    if (p && bytes > 0) {
+        s.lo = reinterpret_cast<uintptr_t>(p);
+        s.hi = s.lo + static_cast<uintptr_t>(bytes);
+    }
+    return s;
+}
+
+bool overlaps(const Span& a, const Span& b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool head_dim_ok(int64_t d) { return d == 64 || d == 128; }
+
+int check_common(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int dtype) {
+    if (dtype != GRET_DTYPE_F32 && dtype != GRET_DTYPE_BF16) return GRET_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || N < 1) return GRET_ERR_SHAPE;
+    if (B > kMaxElems || H > kMaxElems / B || N > kMaxElems / (B * H)) return GRET_ERR_SHAPE;
+    if (B * H * N > kMaxElems / 128) return GRET_ERR_SHAPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GRET_ERR_UNSUPPORTED;
+    return GRET_OK;
+}
+
+// Plan used for both workspace sizing (G at its cap) and launching (G chosen
+// from the device).
+SegPlan make_plan(int64_t B, int64_t H, int64_t N, int64_t chunk, int64_t G) {
+    SegPlan p;
+    p.BH = B * H;
+    p.nc = (N + chunk - 1) / chunk;
+    p.T = p.BH * p.nc;
+    p.G = G < 1 ? 1 : (G > p.T ? p.T : G);
+    p.max_seg = gret::seg_max_per_head(p.BH, p.nc, p.G);
+    return p;
+}
+
+size_t workspace_need(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                      int dtype) {
+    if (dtype != GRET_DTYPE_BF16) return 0;
+    const SegPlan cap = make_plan(B, H, N, chunk, gret::kMaxPrefillGroups);
+    return gret::bf16_workspace_layout(cap, dk, dv).bytes;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GRET_OK : GRET_ERR_HIP; }
+
+}  // namespace
+
+namespace gret {
+
+PrefillWorkspace bf16_workspace_layout(const SegPlan& p, int64_t dk, int64_t dv) {
+    PrefillWorkspace w;
+    const size_t slots = static_cast<size_t>(p.BH) * static_cast<size_t>(p.max_seg);
+    w.state_off = 0;
+    w.meta_off = slots * static_cast<size_t>(dk * dv) * sizeof(float);
+    w.bytes = w.meta_off + slots * 2 * sizeof(float);
+    w.bytes = (w.bytes + 255) & ~size_t(255);
+    return w;
+}
+
+}  // namespace gret
+
+extern "C" {
+
+const char* gret_status_string(int status) {
+    switch (status) {
+        case GRET_OK: return "GRET_OK: success";
+        case GRET_ERR_NULL: return "GRET_ERR_NULL: a required pointer is NULL";
+        case GRET_ERR_SHAPE: return "GRET_ERR_SHAPE: B, H or N is < 1 or the sizes overflow";
+        case GRET_ERR_UNSUPPORTED:
+            return "GRET_ERR_UNSUPPORTED: dk/dv not in {64,128}, chunk not in {64,128,256}, "
+                   "unknown dtype, or a tensor pointer not 16-byte aligned";
+        case GRET_ERR_ALIAS:
+            return "GRET_ERR_ALIAS: out overlaps another buffer, or the states overlap without "
+                   "being identical";
+        case GRET_ERR_HIP: return "GRET_ERR_HIP: a HIP runtime call or kernel launch failed";
+        case GRET_ERR_WORKSPACE:
+            return "GRET_ERR_WORKSPACE: workspace missing, smaller than "
+                   "gret_prefill_workspace_bytes() or not 256-byte aligned";
+        default: return "unknown gret status";
+    }
+}
+
+int gret_prefill_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                                 int64_t chunk, int dtype, size_t* bytes) {
+    if (!bytes) return GRET_ERR_NULL;
+    int st = check_common(B, H, N, dk, dv, dtype);
+    if (st != GRET_OK) return st;
+    if (chunk != 64 && chunk != 128 && chunk != 256) return GRET_ERR_UNSUPPORTED;
+    *bytes = workspace_need(B, H, N, dk, dv, chunk, dtype);
+    return GRET_OK;
+}
+
+int gret_prefill(const void* q, const void* k, const void* v, const float* log_gamma,
+                 const float* state_in, void* out, float* state_out, int64_t B, int64_t H,
+                 int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !log_gamma || !out) return GRET_ERR_NULL;
+    int st = check_common(B, H, N, dk, dv, dtype);
+    if (st != GRET_OK) return st;
+    if (chunk != 64 && chunk != 128 && chunk != 256) return GRET_ERR_UNSUPPORTED;
+    for (const void* p : {q, k, v, (const void*)out, (const void*)state_in, (const void*)state_out})
+        if (p && !aligned(p, 16)) return GRET_ERR_UNSUPPORTED;
+    if (!aligned(log_gamma, 4)) return GRET_ERR_UNSUPPORTED;
+
+    const int64_t esz = dtype == GRET_DTYPE_BF16 ? 2 : 4;
+    const int64_t BHN = B * H * N;
+    const size_t need = workspace_need(B, H, N, dk, dv, chunk, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return GRET_ERR_WORKSPACE;
+
+    const Span sq = span_of(q, BHN * dk * esz), sk = span_of(k, BHN * dk * esz),
+               sv = span_of(v, BHN * dv * esz), sl = span_of(log_gamma, BHN * 4),
+               so = span_of(out, BHN * dv * esz),
+               si = span_of(state_in, B * H * dk * dv * 4),
+               ss = span_of(state_out, B * H * dk * dv * 4),
+               sw = span_of(workspace, need > 0 ? (int64_t)need : 0);
+    for (const Span& x : {sq, sk, sv, sl, si, ss, sw})
+        if (overlaps(so, x)) return GRET_ERR_ALIAS;
+    for (const Span& x : {sq, sk, sv, sl, sw})
+        if (overlaps(ss, x)) return GRET_ERR_ALIAS;
+    if (overlaps(ss, si) && state_out != state_in) return GRET_ERR_ALIAS;
+    for (const Span& x : {sq, sk, sv, sl, si})
+        if (overlaps(sw, x)) return GRET_ERR_ALIAS;
+
+    gret::PrefillArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_gamma = log_gamma;
+    a.state_in = state_in;
+    a.out = out;
+    a.state_out = state_out;
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.dk = dk;
+    a.dv = dv;
+    a.chunk = chunk;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+
+    (void)hipGetLastError();  // clear anything pending from unrelated calls
+    if (dtype == GRET_DTYPE_F32) return hip_status(gret::launch_prefill_f32(a));
+
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GRET_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return GRET_ERR_HIP;
+    const int per_cu = gret::prefill_bf16_blocks_per_cu(dk, dv, chunk);
+    if (per_cu <= 0 || cus <= 0) return GRET_ERR_HIP;
+    int64_t G = static_cast<int64_t>(cus) * per_cu;
+    if (G > gret::kMaxPrefillGroups) G = gret::kMaxPrefillGroups;
+    const SegPlan plan = make_plan(B, H, N, chunk, G);
+    return hip_status(gret::launch_prefill_bf16(a, plan));
+}
+
+int gret_decode_step(const void* q, const void* k, const void* v, const float* log_gamma,
+                     const float* state_in, void* out, float* state_out, int64_t B, int64_t H,
+                     int64_t dk, int64_t dv, int dtype, void* stream) {
+    if (!q || !k || !v || !log_gamma || !out || !state_out) return GRET_ERR_NULL;
+    int st = check_common(B, H, 1, dk, dv, dtype);
+    if (st != GRET_OK) return st;
+    for (const void* p : {q, k, v, (const void*)out, (const void*)state_in, (const void*)state_out})
+        if (p && !aligned(p, 16)) return GRET_ERR_UNSUPPORTED;
+    if (!aligned(log_gamma, 4)) return GRET_ERR_UNSUPPORTED;
+
+    const int64_t esz = dtype == GRET_DTYPE_BF16 ? 2 : 4;
+    const int64_t BH = B * H;
+    const Span sq = span_of(q, BH * dk * esz), sk = span_of(k, BH * dk * esz),
+               sv = span_of(v, BH * dv * esz), sl = span_of(log_gamma, BH * 4),
+               so = span_of(out, BH * dv * esz), si = span_of(state_in, BH * dk * dv * 4),
+               ss = span_of(state_out, BH * dk * dv * 4);
+    for (const Span& x : {sq, sk, sv, sl, si, ss})
+        if (overlaps(so, x)) return GRET_ERR_ALIAS;
+    for (const Span& x : {sq, sk, sv, sl})
+        if (overlaps(ss, x)) return GRET_ERR_ALIAS;
+    if (overlaps(ss, si) && state_out != state_in) return GRET_ERR_ALIAS;
+
+    gret::DecodeArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_gamma = log_gamma;
+    a.state_in = state_in;
+    a.out = out;
+    a.state_out = state_out;
+    a.B = B;
+    a.H = H;
+    a.dk = dk;
+    a.dv = dv;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return hip_status(dtype == GRET_DTYPE_BF16 ? gret::launch_decode_bf16(a)
+                                               : gret::launch_decode_f32(a));
+}
+
+}  // extern "C"

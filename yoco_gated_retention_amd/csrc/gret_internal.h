@@ -1,0 +1,63 @@
+// gret_internal.h -- launch entry points shared between the C ABI layer and
+// the kernel translation units. Not part of the public interface.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gret_segments.h"
+
+namespace gret {
+
+// Log-gate clamp range applied by every kernel (see GRET_LOG_GAMMA_FLOOR).
+constexpr float kLogGammaFloor = -80.0f;
+
+// A segment's incoming state is dropped from outputs once its survival factor
+// exp(B) falls below the smallest normal fp32 number (exp(-87.34)).
+constexpr float kSurvivalDropLog = -88.0f;
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_gamma;
+    const float* state_in;  // may be null
+    void* out;
+    float* state_out;       // may be null
+    int64_t B, H, N, dk, dv, chunk;
+    void* workspace;
+    size_t workspace_bytes;
+    hipStream_t stream;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_gamma;
+    const float* state_in;  // may be null
+    void* out;
+    float* state_out;
+    int64_t B, H, dk, dv;
+    hipStream_t stream;
+};
+
+// Workspace layout of the bf16 (matrix-core) prefill path for a plan.
+struct PrefillWorkspace {
+    size_t state_off;  // float [BH][max_seg][dk*dv]
+    size_t meta_off;   // float2 [BH][max_seg]: (total log-decay, prefix chunks)
+    size_t bytes;
+};
+
+PrefillWorkspace bf16_workspace_layout(const SegPlan& p, int64_t dk, int64_t dv);
+
+// Each returns a hipError_t from the launch (hipSuccess when enqueued).
+hipError_t launch_decode_f32(const DecodeArgs& a);
+hipError_t launch_decode_bf16(const DecodeArgs& a);
+hipError_t launch_prefill_f32(const PrefillArgs& a);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, const SegPlan& plan);
+
+// Workgroups per CU the bf16 prefill kernel can keep resident (0 on error).
+int prefill_bf16_blocks_per_cu(int64_t dk, int64_t dv, int64_t chunk);
+
+}  // namespace gret
