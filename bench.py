@@ -182,7 +182,21 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=1)
     ap.add_argument("--sweep", action="store_true",
                     help="also time chunk 64/128/256 on the 32K and 512K workloads (stderr)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 1 GiB (x3) to calibrate the HBM "
+                         "traffic counters")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": src.numel() * 2,
+                          "calibrate_copy_bytes_written": dst.numel() * 2, "copies": 3}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(heads and sequences shard across GPUs without communication; see DESIGN.md). "

@@ -66,7 +66,8 @@ typedef enum {
     GRET_OK = 0,
     GRET_ERR_NULL = 1,        /* a required pointer is NULL                   */
     GRET_ERR_SHAPE = 2,       /* B, H or N < 1, or sizes overflow             */
-    GRET_ERR_UNSUPPORTED = 3, /* dk, dv, chunk or dtype outside the set below */
+    GRET_ERR_UNSUPPORTED = 3, /* dk, dv, chunk or dtype outside the set below,
+                                 or a tensor pointer not 16-byte aligned      */
     GRET_ERR_ALIAS = 4,       /* out overlaps an input, or states overlap
                                  without being identical                      */
     GRET_ERR_HIP = 5,         /* a HIP runtime call or launch failed          */
@@ -108,7 +109,9 @@ int gret_prefill_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, in
  *   state_out           fp32 [B,H,dk,dv] or NULL; may be identical to state_in
  *                       (in place); any other overlap is GRET_ERR_ALIAS
  *   B, H, N             >= 1; N need not be a multiple of chunk (the tail chunk
- *                       is masked and state_out is exactly S_{N-1})
+ *                       is masked and state_out is exactly S_{N-1}); with
+ *                       dtype BF16, N <= 2^23 (one head's rows are addressed
+ *                       with 32-bit offsets), else GRET_ERR_SHAPE
  *   dk, dv              64 or 128
  *   chunk               64, 128 or 256 -- the chunk length of the chunkwise form
  *   dtype               gret_dtype_t of q, k, v, out

@@ -14,6 +14,8 @@ namespace {
 using gret::SegPlan;
 
 constexpr int64_t kMaxElems = int64_t(1) << 50;  // guards size arithmetic
+// The bf16 prefill addresses one head's rows through 32-bit buffer offsets.
+constexpr int64_t kMaxBf16PrefillN = int64_t(1) << 23;
 
 struct Span {
     uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -121,6 +123,7 @@ int gret_prefill(const void* q, const void* k, const void* v, const float* log_g
     int st = check_common(B, H, N, dk, dv, dtype);
     if (st != GRET_OK) return st;
     if (chunk != 64 && chunk != 128 && chunk != 256) return GRET_ERR_UNSUPPORTED;
+    if (dtype == GRET_DTYPE_BF16 && N > kMaxBf16PrefillN) return GRET_ERR_SHAPE;
     for (const void* p : {q, k, v, (const void*)out, (const void*)state_in, (const void*)state_out})
         if (p && !aligned(p, 16)) return GRET_ERR_UNSUPPORTED;
     if (!aligned(log_gamma, 4)) return GRET_ERR_UNSUPPORTED;

@@ -23,8 +23,8 @@
 //               running log-decay from the segment start drops below
 //               kSurvivalDropLog (the incoming state's survival factor is then
 //               below the smallest normal fp32 number), and from there on
-//               computes outputs too. Log-gates are <= 0, so the running sum
-//               only decreases and every later output has a smaller factor.
+//               stores outputs too. Log-gates are <= 0, so the running sum only
+//               decreases and every later output has a smaller factor.
 //   2. combine: per head, chain the segment maps in order, leaving each
 //               segment's incoming state in its workspace slot; the last one
 //               is the final state.
@@ -33,17 +33,18 @@
 // Each output is written exactly once and inputs are read about once (the
 // leading chunks twice).
 //
-// Per-workgroup data flow (256 threads = 4 wavefronts, wave w owns value
-// columns [w*DV/4, (w+1)*DV/4)), per 64-position tile of a chunk:
-//   global -> registers (prefetched one tile ahead) -> LDS: Q and K row-major,
-//   K and V transposed (dim-major) so the position index is contiguous, which
-//   is what the matrix-core operand layout needs for contractions over
-//   positions. The state S stays in registers as fp32 accumulator tiles;
-//   wave w holds S[:, its columns].
-//   * scores   P^T = K Q^T for the wave's 16 query rows (16x16x32 bf16 MFMA),
-//              decay mask exp(beta_j - beta_l) in fp32, cast to bf16 into LDS;
-//   * output   O^T = S^T Q^T (S taken straight from the accumulator registers)
-//              scaled by exp(beta_j), plus V^T P~^T, so each lane ends with 4
+// Workgroup layout: DV/16 wavefronts (8 at dv = 128, two per SIMD); wave w
+// owns value columns [16w, 16w+16) of the state and of the output. Per
+// 64-position tile:
+//   global -> registers (prefetched one tile ahead, range-checked buffer
+//   loads) -> LDS, Q, K and V row-major with an XOR swizzle of 16-byte chunks.
+//   Operands whose contraction runs over positions (K^T, V^T) are read with
+//   the gfx950 transposing LDS load ds_read_b64_tr_b16, so no transposed copy
+//   is ever made. The state stays in registers as fp32 accumulator tiles.
+//   * scores   P^T = K Q^T per 16x16 tile (16x16x32 bf16 MFMA), decay mask
+//              exp(beta_j - beta_l) in fp32, cast to bf16 into LDS;
+//   * output   O^T = S^T Q^T (S straight from the accumulator registers)
+//              scaled by exp(beta_j), plus V^T P~^T; each lane ends with 4
 //              consecutive output columns of one row and stores 8 bytes;
 //   * state    S = exp(g) S + K^T (Gamma V) with Gamma_l = exp(g - beta_l).
 #include <hip/hip_runtime.h>
@@ -54,20 +55,53 @@
 namespace gret {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTile = 64;    // positions per tile
-constexpr int kPadQ = 8;     // bf16 padding per row of row-major tiles (16 bytes)
-constexpr int kPadT = 8;     // bf16 padding per row of transposed tiles
+constexpr int kTile = 64;  // positions per tile
+constexpr int kPadP = 8;   // bf16 padding per row of the score tile
 
 __device__ inline f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 __device__ inline bf16x8 lds_read8(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ inline bf16x4 lds_read4(const bf16_t* p) { return *reinterpret_cast<const bf16x4*>(p); }
 
+// Transposing LDS read: within each 16-lane group, lane l receives element
+// (l % 4) of the 8-byte pieces addressed by lanes 4e + l/4 (e = 0..3). With
+// lane s pointing at row t0 + s/4, column n0 + 4(s % 4) of a row-major tile,
+// lane l gets column n0 + l of rows t0..t0+3.
+__device__ inline bf16x4 lds_read_tr4(const bf16_t* p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
 __device__ inline bf16x8 cat44(const bf16x4& a, const bf16x4& b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Range-checked buffer access (CDNA buffer resources). A descriptor covers one
+// head's rows; a load past its end returns zeros and a store past it is
+// dropped by the hardware, which is exactly the tail masking the chunkwise form
+// needs (padded positions carry zero K and V and log-gate 0, and their outputs
+// are not written), without a branch on the hot path.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, gfx9-family data format
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
+}
+__device__ inline bf16x8 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+    return __builtin_bit_cast(bf16x8, v);
+}
+__device__ inline float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+__device__ inline void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, const bf16x4& v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), r, byte_off, 0, 0);
 }
 
 struct Params {
@@ -78,44 +112,67 @@ struct Params {
     const float* state_in;
     bf16_t* out;
     float* state_out;
-    float* ws_state;   // [BH][max_seg][DK*DV]
-    float2* ws_meta;   // [BH][max_seg]: (total log-decay, leading chunks)
+    float* ws_state;  // [BH][max_seg][DK*DV]
+    float2* ws_meta;  // [BH][max_seg]: (total log-decay, leading chunks)
     SegPlan plan;
     int64_t N;
+};
+
+// Per-head views of the prefill tensors.
+struct HeadRsrc {
+    __amdgpu_buffer_rsrc_t q, k, v, lg, out;
 };
 
 template <int DK, int DV, int R>
 struct Cfg {
     static constexpr int C = kTile * R;
-    static constexpr int CW = DV / 4;       // value columns per wave
-    static constexpr int TC = CW / 16;      // 16-wide column tiles per wave
+    static constexpr int NW = DV / 16;      // wavefronts; wave w owns value columns 16w..16w+15
+    static constexpr int NT = 64 * NW;      // threads per workgroup
     static constexpr int TK = DK / 16;      // 16-row key tiles of the state
     static constexpr int KS = DK / 32;      // k-steps over dk
-    static constexpr int QP = DK + kPadQ;   // row pitch (elements) of Qs / Ks
-    static constexpr int TP = kTile + kPadT;  // row pitch of Kts / Vts / Ps
-    static constexpr int KBLK = 16 * (DK / 8);  // 4x8 staging blocks per K tile
-    static constexpr int VBLK = 16 * (DV / 8);
-    static constexpr int QLD = kTile * DK / 8 / kThreads;  // 16-byte Q loads per thread
-    static_assert(TC >= 1 && TK >= 1 && KS >= 1, "tile shape");
-    static_assert(KBLK <= kThreads && VBLK <= kThreads, "one staging block per thread");
-    static_assert(QLD >= 1 && QLD * kThreads * 8 == kTile * DK, "Q staging");
+    static constexpr int QCH = DK / 8;      // 16-byte chunks per Q/K row
+    static constexpr int VCH = DV / 8;      // 16-byte chunks per V row
+    static constexpr int QLD = kTile * QCH / NT;  // staged chunks per thread
+    static constexpr int VLD = kTile * VCH / NT;
+    static constexpr int PP = kTile + kPadP;  // row pitch (elements) of the score tile
+    static constexpr int BSTEP = NW / 4;      // score tiles: waves per query block
+    static_assert(QLD >= 1 && QLD * NT == kTile * QCH, "Q/K staging");
+    static_assert(VLD >= 1 && VLD * NT == kTile * VCH, "V staging");
+    static_assert(QCH >= 8 && VCH >= 8, "swizzle spans 8 chunks");
+    static_assert(NW == 4 || NW == 8, "waves");
+    static_assert(NT == DV * 4, "threads");
 };
+
+// Threads per workgroup for a value width (one wavefront per 16 columns).
+template <int DV>
+constexpr int kThreadsFor = DV * 4;
+
+// XOR swizzle of the 16-byte chunks of a row-major tile row. Reads of 8
+// consecutive rows at one chunk hit 8 different chunk slots, and the 4 rows x
+// 2 chunks touched by one 16-lane group of a transposing read map to 8
+// different slots, so both access patterns are free of bank conflicts.
+__device__ inline int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+
+// Element offset of (row, col) in a swizzled row-major tile with D columns.
+template <int D>
+__device__ inline int toff(int row, int col) {
+    return row * D + (((col >> 3) ^ swz(row)) << 3) + (col & 7);
+}
 
 template <int DK, int DV, int R>
 struct __attribute__((aligned(16))) Smem {
     using c = Cfg<DK, DV, R>;
-    bf16_t qs[kTile * c::QP];
-    bf16_t ks[kTile * c::QP];
-    bf16_t kts[DK * c::TP];
-    bf16_t vts[DV * c::TP];
-    bf16_t ps[kTile * c::TP];
+    bf16_t qs[kTile * DK];
+    bf16_t ks[kTile * DK];
+    bf16_t vs[kTile * DV];
+    bf16_t ps[kTile * c::PP];
     float beta[c::C];
 };
 
 template <int DK, int DV>
 struct __attribute__((aligned(16))) Smem2 {  // earlier tiles of the chunk (chunks > 64)
-    bf16_t ks[kTile * (DK + kPadQ)];
-    bf16_t vts[DV * (kTile + kPadT)];
+    bf16_t ks[kTile * DK];
+    bf16_t vs[kTile * DV];
 };
 
 // All LDS of one workgroup; the restaging buffers exist only for chunks > 64.
@@ -136,105 +193,56 @@ template <int DK, int DV, int R>
 struct TileRegs {
     using c = Cfg<DK, DV, R>;
     bf16x8 q[c::QLD];
-    bf16x8 k[4];
-    bf16x8 v[4];
-    float ell[R];  // wave 0: log-gates of the chunk (lane holds R consecutive)
+    bf16x8 k[c::QLD];
+    bf16x8 v[c::VLD];
+    float ell[R];  // log-gates of the chunk (lane holds R consecutive)
 };
 
-// Loads tile `tile_pos` (first position of the tile, < N) of head x; Q only
-// when WITH_Q, the chunk's log-gates only when chunk_start.
+// Loads tile `tile_pos` of a head (Q only when WITH_Q) plus the log-gates of
+// the chunk starting at chunk_pos. Positions past the end read as zero.
 template <int DK, int DV, int R, bool WITH_Q = true>
-__device__ inline void load_tile(const Params& p, int64_t x, int64_t tile_pos, bool chunk_start,
-                                 int64_t chunk_pos, TileRegs<DK, DV, R>& t) {
+__device__ inline void load_tile(const HeadRsrc& hr, uint32_t tile_pos, uint32_t chunk_pos,
+                                 TileRegs<DK, DV, R>& t) {
     using c = Cfg<DK, DV, R>;
     const int tid = threadIdx.x;
-    const int64_t N = p.N;
-    const bf16x8 zero = {};
-    // Q: row-major, thread covers rows tid/(DK/8) + i*(256/(DK/8)), one 16-byte piece
-    if (WITH_Q) {
-        constexpr int PER_ROW = DK / 8;
-        constexpr int ROWS_PER_PASS = kThreads / PER_ROW;
-        const int col = (tid % PER_ROW) * 8;
-#pragma unroll
-        for (int i = 0; i < c::QLD; ++i) {
-            const int row = tid / PER_ROW + i * ROWS_PER_PASS;
-            const int64_t pos = tile_pos + row;
-            t.q[i] = pos < N ? *reinterpret_cast<const bf16x8*>(p.q + (x * N + pos) * DK + col)
-                             : zero;
-        }
-    }
-    // K: 4 positions x 8 dims per thread (position quad fastest across lanes)
-    if (tid < c::KBLK) {
-        const int pq = tid % 16, c8 = tid / 16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t pos = tile_pos + 4 * pq + i;
-            t.k[i] = pos < N ? *reinterpret_cast<const bf16x8*>(p.k + (x * N + pos) * DK + 8 * c8)
-                             : zero;
-        }
-    }
-    if (tid < c::VBLK) {
-        const int pq = tid % 16, c8 = tid / 16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t pos = tile_pos + 4 * pq + i;
-            t.v[i] = pos < N ? *reinterpret_cast<const bf16x8*>(p.v + (x * N + pos) * DV + 8 * c8)
-                             : zero;
-        }
-    }
-    if (chunk_start && tid < 64) {
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const int64_t pos = chunk_pos + tid * R + i;
-            // positions past the end decay nothing (gate 1) and carry zero K, V
-            t.ell[i] = pos < N ? clamp_log_gamma(p.log_gamma[x * N + pos], kLogGammaFloor) : 0.0f;
-        }
-    }
-}
-
-template <int DK, int DV, int R>
-__device__ inline void write_kv(const TileRegs<DK, DV, R>& t, bf16_t* ks, bf16_t* kts,
-                                bf16_t* vts) {
-    using c = Cfg<DK, DV, R>;
-    const int tid = threadIdx.x;
-    if (tid < c::KBLK) {
-        const int pq = tid % 16, c8 = tid / 16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<bf16x8*>(ks + (4 * pq + i) * c::QP + 8 * c8) = t.k[i];
-        if (kts) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16x4 col = {t.k[0][e], t.k[1][e], t.k[2][e], t.k[3][e]};
-                *reinterpret_cast<bf16x4*>(kts + (8 * c8 + e) * c::TP + 4 * pq) = col;
-            }
-        }
-    }
-    if (tid < c::VBLK) {
-        const int pq = tid % 16, c8 = tid / 16;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bf16x4 col = {t.v[0][e], t.v[1][e], t.v[2][e], t.v[3][e]};
-            *reinterpret_cast<bf16x4*>(vts + (8 * c8 + e) * c::TP + 4 * pq) = col;
-        }
-    }
-}
-
-template <int DK, int DV, int R>
-__device__ inline void write_q(const TileRegs<DK, DV, R>& t, bf16_t* qs) {
-    using c = Cfg<DK, DV, R>;
-    constexpr int PER_ROW = DK / 8;
-    constexpr int ROWS_PER_PASS = kThreads / PER_ROW;
-    const int tid = threadIdx.x;
-    const int col = (tid % PER_ROW) * 8;
 #pragma unroll
     for (int i = 0; i < c::QLD; ++i) {
-        const int row = tid / PER_ROW + i * ROWS_PER_PASS;
-        *reinterpret_cast<bf16x8*>(qs + row * c::QP + col) = t.q[i];
+        const int id = tid + i * c::NT;
+        const uint32_t off = ((tile_pos + id / c::QCH) * DK + (id % c::QCH) * 8) * 2;
+        if constexpr (WITH_Q) t.q[i] = buf_load8(hr.q, off);
+        t.k[i] = buf_load8(hr.k, off);
+    }
+#pragma unroll
+    for (int i = 0; i < c::VLD; ++i) {
+        const int id = tid + i * c::NT;
+        t.v[i] = buf_load8(hr.v, ((tile_pos + id / c::VCH) * DV + (id % c::VCH) * 8) * 2);
+    }
+    const uint32_t lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < R; ++i) t.ell[i] = buf_load_f32(hr.lg, (chunk_pos + lane * R + i) * 4);
+}
+
+template <int DK, int DV, int R, bool WITH_Q = true>
+__device__ inline void write_tile(const TileRegs<DK, DV, R>& t, bf16_t* qs, bf16_t* ks,
+                                  bf16_t* vs) {
+    using c = Cfg<DK, DV, R>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < c::QLD; ++i) {
+        const int id = tid + i * c::NT;
+        const int o = toff<DK>(id / c::QCH, (id % c::QCH) * 8);
+        if constexpr (WITH_Q) *reinterpret_cast<bf16x8*>(qs + o) = t.q[i];
+        *reinterpret_cast<bf16x8*>(ks + o) = t.k[i];
+    }
+#pragma unroll
+    for (int i = 0; i < c::VLD; ++i) {
+        const int id = tid + i * c::NT;
+        *reinterpret_cast<bf16x8*>(vs + toff<DV>(id / c::VCH, (id % c::VCH) * 8)) = t.v[i];
     }
 }
 
-// Wave 0: chunk-local inclusive prefix sum of the log-gates into beta[C].
+// Wave 0: chunk-local inclusive prefix sum of the clamped log-gates into
+// beta[C] (positions past the end read as log-gate 0).
 template <int DK, int DV, int R>
 __device__ inline void scan_beta(const TileRegs<DK, DV, R>& t, float* beta) {
     const int tid = threadIdx.x;
@@ -243,10 +251,9 @@ __device__ inline void scan_beta(const TileRegs<DK, DV, R>& t, float* beta) {
     float run = 0.0f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-        run += t.ell[i];
+        run += clamp_log_gamma(t.ell[i], kLogGammaFloor);
         loc[i] = run;
     }
-    // inclusive scan of lane totals across the wavefront
     float tot = run;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -258,44 +265,95 @@ __device__ inline void scan_beta(const TileRegs<DK, DV, R>& t, float* beta) {
     for (int i = 0; i < R; ++i) beta[tid * R + i] = excl + loc[i];
 }
 
+// 8 consecutive positions t0..t0+7 of column col0 + l (l = this lane's index
+// in its 16-lane group) from a row-major swizzled tile with D columns: the
+// MFMA operand for a contraction over positions.
+template <int D>
+__device__ inline bf16x8 read_cols8(const bf16_t* tile, int t0, int col0) {
+    const int s = threadIdx.x & 15;
+    const int row = t0 + (s >> 2);
+    const int col = col0 + 4 * (s & 3);
+    const bf16x4 a = lds_read_tr4(tile + toff<D>(row, col));
+    const bf16x4 b = lds_read_tr4(tile + toff<D>(row + 4, col));
+    return cat44(a, b);
+}
+
 // Per-thread state of one segment's pass.
 template <int DK, int DV, int R>
 struct Acc {
     using c = Cfg<DK, DV, R>;
-    f32x4 s[c::TK][c::TC];   // S[16tk + 4g + i][wave cols 16tc + li]
-    f32x4 ds[R > 1 ? c::TK : 1][R > 1 ? c::TC : 1];  // chunk increment (chunks > 64)
+    f32x4 s[c::TK];                    // S[16tk + 4g + i][16w + li]
+    f32x4 ds[R > 1 ? c::TK : 1];       // chunk increment (chunks > 64)
 };
 
-// Stages K (row-major) and V (transposed) of an earlier tile of the current
-// chunk (positions pos..pos+63) into s2; its transposed K is never needed.
+// Stages K and V of an earlier tile of the current chunk into s2.
 template <int DK, int DV, int R>
-__device__ inline void restage(const Params& p, int64_t x, int64_t pos, Smem2<DK, DV>& s2) {
+__device__ inline void restage(const HeadRsrc& hr, uint32_t pos, Smem2<DK, DV>& s2) {
     TileRegs<DK, DV, R> t;
-    load_tile<DK, DV, R, false>(p, x, pos, false, 0, t);
-    write_kv<DK, DV, R>(t, s2.ks, nullptr, s2.vts);
+    load_tile<DK, DV, R, false>(hr, pos, pos, t);
+    write_tile<DK, DV, R, false>(t, nullptr, s2.ks, s2.vs);
 }
 
-// Scores for the wave's 16 query rows (j-block w) against key tile `kt` (K
-// row-major in `ksrc`), decayed and written as bf16 to sm.ps[j][l].
+// Cross-chunk term O^T = S^T Q^T for the 64 rows of the tile, then row j scaled
+// by exp(beta_j). The state tile pair (2m, 2m+1) gives each lane
+// dk = 32m + {4g..4g+3, 16+4g..16+4g+3}; the Q operand is read with the same
+// permutation of dk, so the contraction pairs matching indices.
+template <int DK, int DV, int R>
+__device__ inline void cross_term(const Smem<DK, DV, R>& sm, const Acc<DK, DV, R>& a, int r,
+                                  f32x4 (&o)[4]) {
+    using c = Cfg<DK, DV, R>;
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) o[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < c::KS; ++m) {
+        const f32x4 lo4 = a.s[2 * m], hi4 = a.s[2 * m + 1];
+        const bf16x8 sf = {to_bf16(lo4[0]), to_bf16(lo4[1]), to_bf16(lo4[2]), to_bf16(lo4[3]),
+                           to_bf16(hi4[0]), to_bf16(hi4[1]), to_bf16(hi4[2]), to_bf16(hi4[3])};
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            const int row = 16 * jt + li;
+            const bf16x8 qf = cat44(lds_read4(sm.qs + toff<DK>(row, 32 * m + 4 * g)),
+                                    lds_read4(sm.qs + toff<DK>(row, 32 * m + 16 + 4 * g)));
+            o[jt] = mfma16(sf, qf, o[jt]);
+        }
+    }
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+        const float f = __expf(sm.beta[kTile * r + 16 * jt + li]);
+        o[jt][0] *= f;
+        o[jt][1] *= f;
+        o[jt][2] *= f;
+        o[jt][3] *= f;
+    }
+}
+
+// Decayed scores of query tile r against key tile t of the chunk, written as
+// bf16 to sm.ps[j][l]. Wave w computes the 16x16 blocks (jb, b) with
+// jb = w / BSTEP and b = w % BSTEP, w % BSTEP + BSTEP, ...; blocks above the
+// diagonal (diag only) are written as zeros.
 template <int DK, int DV, int R>
 __device__ inline void scores_to_lds(Smem<DK, DV, R>& sm, const bf16_t* ksrc, int r, int t,
                                      bool diag) {
     using c = Cfg<DK, DV, R>;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int li = lane & 15, g = lane >> 4;
-    const int jrow = 16 * w + li;                 // row within the tile
+    const int jb = w / c::BSTEP;
+    const int jrow = 16 * jb + li;
     const float bj = sm.beta[kTile * r + jrow];
     bf16x8 qf[c::KS];
 #pragma unroll
-    for (int ks = 0; ks < c::KS; ++ks) qf[ks] = lds_read8(sm.qs + jrow * c::QP + 32 * ks + 8 * g);
+    for (int ks = 0; ks < c::KS; ++ks) qf[ks] = lds_read8(sm.qs + toff<DK>(jrow, 32 * ks + 8 * g));
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b0 = 0; b0 < 4; b0 += c::BSTEP) {
+        const int b = b0 + w % c::BSTEP;
         bf16x4 pk;
-        if (!diag || b <= w) {
+        if (!diag || b <= jb) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < c::KS; ++ks) {
-                const bf16x8 kf = lds_read8(ksrc + (16 * b + li) * c::QP + 32 * ks + 8 * g);
+                const bf16x8 kf = lds_read8(ksrc + toff<DK>(16 * b + li, 32 * ks + 8 * g));
                 acc = mfma16(kf, qf[ks], acc);
             }
             // acc[i] = P^T[l = 16b + 4g + i][j = jrow]
@@ -309,79 +367,139 @@ __device__ inline void scores_to_lds(Smem<DK, DV, R>& sm, const bf16_t* ksrc, in
         } else {
             pk = bf16x4{};
         }
-        *reinterpret_cast<bf16x4*>(sm.ps + jrow * c::TP + 16 * b + 4 * g) = pk;
+        *reinterpret_cast<bf16x4*>(sm.ps + jrow * c::PP + 16 * b + 4 * g) = pk;
     }
 }
 
-// O^T[cols][rows] += V_t^T P~^T over the positions of tile t.
+// O^T[cols][rows] += V_t^T P~^T over the positions of tile t (V read transposed).
 template <int DK, int DV, int R>
-__device__ inline void apply_scores(Smem<DK, DV, R>& sm, const bf16_t* vtsrc, bool diag,
-                                    f32x4 (&o)[4][Cfg<DK, DV, R>::TC]) {
+__device__ inline void apply_scores(const Smem<DK, DV, R>& sm, const bf16_t* vsrc, bool diag,
+                                    f32x4 (&o)[4]) {
     using c = Cfg<DK, DV, R>;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int li = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 vf[c::TC];
-#pragma unroll
-        for (int tc = 0; tc < c::TC; ++tc)
-            vf[tc] = lds_read8(vtsrc + (c::CW * w + 16 * tc + li) * c::TP + 32 * ks + 8 * g);
+        const bf16x8 vf = read_cols8<DV>(vsrc, 32 * ks + 8 * g, 16 * w);
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             if (diag && 2 * ks > jt) continue;  // whole 32-position step is above the diagonal
-            const bf16x8 pf = lds_read8(sm.ps + (16 * jt + li) * c::TP + 32 * ks + 8 * g);
-#pragma unroll
-            for (int tc = 0; tc < c::TC; ++tc) o[jt][tc] = mfma16(vf[tc], pf, o[jt][tc]);
+            const bf16x8 pf = lds_read8(sm.ps + (16 * jt + li) * c::PP + 32 * ks + 8 * g);
+            o[jt] = mfma16(vf, pf, o[jt]);
         }
     }
 }
 
 template <int DK, int DV, int R>
-__device__ inline void store_out(const Params& p, int64_t x, int64_t tile_pos,
-                                 f32x4 (&o)[4][Cfg<DK, DV, R>::TC]) {
-    using c = Cfg<DK, DV, R>;
+__device__ inline void store_out(const __amdgpu_buffer_rsrc_t& out, uint32_t tile_pos,
+                                 const f32x4 (&o)[4]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int li = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
-        const int64_t pos = tile_pos + 16 * jt + li;
-        if (pos >= p.N) continue;
+        const uint32_t pos = tile_pos + 16 * jt + li;
+        const bf16x4 pk = {to_bf16(o[jt][0]), to_bf16(o[jt][1]), to_bf16(o[jt][2]),
+                           to_bf16(o[jt][3])};
+        buf_store4(out, (pos * DV + 16 * w + 4 * g) * 2, pk);
+    }
+}
+
+// acc += K^T (Gamma V) over the current tile, Gamma_l = exp(gc - beta_l); K and
+// V are read transposed so that positions are the contraction index.
+template <int DK, int DV, int R>
+__device__ inline void state_update(const Smem<DK, DV, R>& sm, int r, float gc,
+                                    f32x4 (&acc)[Cfg<DK, DV, R>::TK]) {
+    using c = Cfg<DK, DV, R>;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = lane >> 4;
 #pragma unroll
-        for (int tc = 0; tc < c::TC; ++tc) {
-            bf16x4 pk = {to_bf16(o[jt][tc][0]), to_bf16(o[jt][tc][1]), to_bf16(o[jt][tc][2]),
-                         to_bf16(o[jt][tc][3])};
-            *reinterpret_cast<bf16x4*>(p.out + (x * p.N + pos) * DV + c::CW * w + 16 * tc + 4 * g) =
-                pk;
+    for (int ks = 0; ks < 2; ++ks) {
+        const int t0 = 32 * ks + 8 * g;
+        const bf16x8 vf = read_cols8<DV>(sm.vs, t0, 16 * w);
+        bf16x8 bf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            bf[e] = to_bf16(from_bf16(vf[e]) * __expf(gc - sm.beta[kTile * r + t0 + e]));
+#pragma unroll
+        for (int tk = 0; tk < c::TK; ++tk) {
+            const bf16x8 kf = read_cols8<DK>(sm.ks, t0, 16 * tk);
+            acc[tk] = mfma16(kf, bf, acc[tk]);
         }
     }
 }
 
-// S (or dS) += K_t^T (Gamma V_t) for the current tile; Gamma_l = exp(gc - beta_l).
 template <int DK, int DV, int R>
-__device__ inline void state_update(Smem<DK, DV, R>& sm, int r, float gc,
-                                    f32x4 (&acc)[Cfg<DK, DV, R>::TK][Cfg<DK, DV, R>::TC]) {
+__device__ inline HeadRsrc head_rsrc(const Params& p, int64_t x) {
+    const int64_t N = p.N;
+    HeadRsrc hr;
+    hr.q = make_rsrc(p.q + x * N * DK, static_cast<uint32_t>(N * DK * 2));
+    hr.k = make_rsrc(p.k + x * N * DK, static_cast<uint32_t>(N * DK * 2));
+    hr.v = make_rsrc(p.v + x * N * DV, static_cast<uint32_t>(N * DV * 2));
+    hr.lg = make_rsrc(p.log_gamma + x * N, static_cast<uint32_t>(N * 4));
+    hr.out = make_rsrc(p.out + x * N * DV, static_cast<uint32_t>(N * DV * 2));
+    return hr;
+}
+
+template <int DK, int DV, int R>
+__device__ inline void scale_state(Acc<DK, DV, R>& a, float eg) {
     using c = Cfg<DK, DV, R>;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int li = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        float gam[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gam[e] = __expf(gc - sm.beta[kTile * r + 32 * ks + 8 * g + e]);
-        bf16x8 bf[c::TC];
-#pragma unroll
-        for (int tc = 0; tc < c::TC; ++tc) {
-            const bf16x8 vf = lds_read8(sm.vts + (c::CW * w + 16 * tc + li) * c::TP + 32 * ks + 8 * g);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bf[tc][e] = to_bf16(from_bf16(vf[e]) * gam[e]);
-        }
-#pragma unroll
-        for (int tk = 0; tk < c::TK; ++tk) {
-            const bf16x8 kf = lds_read8(sm.kts + (16 * tk + li) * c::TP + 32 * ks + 8 * g);
-#pragma unroll
-            for (int tc = 0; tc < c::TC; ++tc) acc[tk][tc] = mfma16(kf, bf[tc], acc[tk][tc]);
-        }
+    for (int tk = 0; tk < c::TK; ++tk) {
+        a.s[tk][0] *= eg;
+        a.s[tk][1] *= eg;
+        a.s[tk][2] *= eg;
+        a.s[tk][3] *= eg;
     }
+}
+
+// Chunks of 64 positions (one tile per chunk): a branch-free steady-state
+// loop. The next chunk is always prefetched (reads past the head's end return
+// zeros), and in state-only mode the outputs are still computed but stored
+// through a zero-length descriptor, so the hardware drops them. Every
+// iteration therefore issues the same memory operations in the same order,
+// which lets the compiler wait only for the prefetched loads at the top of the
+// loop while the previous chunk's output stores are still in flight.
+template <int DK, int DV, int R>
+__device__ float run_chunks_c64(const Params& p, Smem<DK, DV, R>& sm, int64_t x, int64_t cb,
+                                int64_t ce, bool full_from_start, Acc<DK, DV, R>& a,
+                                int64_t* lead) {
+    static_assert(R == 1, "one tile per chunk");
+    bool full = full_from_start;
+    float total = 0.0f;
+    *lead = full ? 0 : (ce - cb);
+    const HeadRsrc hr = head_rsrc<DK, DV, R>(p, x);
+    const __amdgpu_buffer_rsrc_t drop = make_rsrc(p.out, 0);
+    TileRegs<DK, DV, R> tr;
+    uint32_t pos = static_cast<uint32_t>(cb * kTile);
+    load_tile<DK, DV, R>(hr, pos, pos, tr);
+    {
+        const f32x4 z[4] = {};
+        store_out<DK, DV, R>(drop, 0, z);  // same store pattern as the loop, all dropped
+    }
+    for (int64_t ch = cb; ch < ce; ++ch, pos += kTile) {
+        scan_beta<DK, DV, R>(tr, sm.beta);
+        write_tile<DK, DV, R>(tr, sm.qs, sm.ks, sm.vs);
+        __syncthreads();
+        const float gc = sm.beta[kTile - 1];
+        load_tile<DK, DV, R>(hr, pos + kTile, pos + kTile, tr);
+
+        f32x4 o[4];
+        cross_term<DK, DV, R>(sm, a, 0, o);
+        scores_to_lds<DK, DV, R>(sm, sm.ks, 0, 0, true);
+        __syncthreads();
+        apply_scores<DK, DV, R>(sm, sm.vs, true, o);
+        store_out<DK, DV, R>(full ? hr.out : drop, pos, o);
+
+        scale_state<DK, DV, R>(a, __expf(gc));
+        state_update<DK, DV, R>(sm, 0, gc, a.s);
+        total += gc;
+        if (!full && total < kSurvivalDropLog) {
+            full = true;
+            *lead = ch + 1 - cb;
+        }
+        __syncthreads();  // LDS tiles are rewritten next iteration
+    }
+    return total;
 }
 
 // Runs chunks [cb, ce) of head x. With full_from_start the pass computes
@@ -392,142 +510,76 @@ template <int DK, int DV, int R>
 __device__ float run_chunks(const Params& p, Smem<DK, DV, R>& sm, Smem2<DK, DV>* s2, int64_t x,
                             int64_t cb, int64_t ce, bool full_from_start, Acc<DK, DV, R>& a,
                             int64_t* lead) {
-    using c = Cfg<DK, DV, R>;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int li = lane & 15, g = lane >> 4;
-    (void)w;
-    bool full = full_from_start;
-    float total = 0.0f;
-    *lead = full ? 0 : (ce - cb);
-    if constexpr (R > 1) {
+    if constexpr (R == 1) {
+        (void)s2;
+        return run_chunks_c64<DK, DV, R>(p, sm, x, cb, ce, full_from_start, a, lead);
+    } else {
+        using c = Cfg<DK, DV, R>;
+        bool full = full_from_start;
+        float total = 0.0f;
+        *lead = full ? 0 : (ce - cb);
 #pragma unroll
-        for (int tk = 0; tk < c::TK; ++tk)
-#pragma unroll
-            for (int tc = 0; tc < c::TC; ++tc) a.ds[tk][tc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    TileRegs<DK, DV, R> tr;
-    load_tile<DK, DV, R>(p, x, cb * c::C, true, cb * c::C, tr);
-
-    for (int64_t ch = cb; ch < ce; ++ch) {
-        const int64_t cpos = ch * c::C;
-        const int64_t nvalid = p.N - cpos < c::C ? p.N - cpos : c::C;
-        const int rv = static_cast<int>((nvalid + kTile - 1) / kTile);
-        for (int r = 0; r < rv; ++r) {
-            const int64_t tpos = cpos + kTile * r;
-            if (r == 0) scan_beta<DK, DV, R>(tr, sm.beta);
-            write_q<DK, DV, R>(tr, sm.qs);
-            write_kv<DK, DV, R>(tr, sm.ks, sm.kts, sm.vts);
-            __syncthreads();
-            const float gc = sm.beta[c::C - 1];
-
-            // prefetch the next tile of this pass
-            if (r + 1 < rv) {
-                load_tile<DK, DV, R>(p, x, tpos + kTile, false, 0, tr);
-            } else if (ch + 1 < ce) {
-                load_tile<DK, DV, R>(p, x, cpos + c::C, true, cpos + c::C, tr);
-            }
-
-            if (full) {
-                f32x4 o[4][c::TC];
-#pragma unroll
-                for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-                    for (int tc = 0; tc < c::TC; ++tc) o[jt][tc] = f32x4{0.f, 0.f, 0.f, 0.f};
-                // cross-chunk term O^T = S^T Q^T. The state tile pair (2m, 2m+1)
-                // gives each lane dk = 32m + {4g..4g+3, 16+4g..16+4g+3}; the Q
-                // operand is read with the same permutation of dk.
-#pragma unroll
-                for (int m = 0; m < c::KS; ++m) {
-                    bf16x8 qf[4];
-#pragma unroll
-                    for (int jt = 0; jt < 4; ++jt) {
-                        const bf16_t* qrow = sm.qs + (16 * jt + li) * c::QP + 32 * m + 4 * g;
-                        qf[jt] = cat44(lds_read4(qrow), lds_read4(qrow + 16));
-                    }
-#pragma unroll
-                    for (int tc = 0; tc < c::TC; ++tc) {
-                        const f32x4 lo4 = a.s[2 * m][tc], hi4 = a.s[2 * m + 1][tc];
-                        const bf16x8 sf = {to_bf16(lo4[0]), to_bf16(lo4[1]), to_bf16(lo4[2]),
-                                           to_bf16(lo4[3]), to_bf16(hi4[0]), to_bf16(hi4[1]),
-                                           to_bf16(hi4[2]), to_bf16(hi4[3])};
-#pragma unroll
-                        for (int jt = 0; jt < 4; ++jt) o[jt][tc] = mfma16(sf, qf[jt], o[jt][tc]);
-                    }
+        for (int tk = 0; tk < c::TK; ++tk) a.ds[tk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const HeadRsrc hr = head_rsrc<DK, DV, R>(p, x);
+        TileRegs<DK, DV, R> tr;
+        load_tile<DK, DV, R>(hr, static_cast<uint32_t>(cb * c::C),
+                             static_cast<uint32_t>(cb * c::C), tr);
+        for (int64_t ch = cb; ch < ce; ++ch) {
+            const int64_t cpos = ch * c::C;
+            const int64_t nvalid = p.N - cpos < c::C ? p.N - cpos : c::C;
+            const int rv = static_cast<int>((nvalid + kTile - 1) / kTile);
+            for (int r = 0; r < rv; ++r) {
+                const uint32_t tpos = static_cast<uint32_t>(cpos + kTile * r);
+                if (r == 0) scan_beta<DK, DV, R>(tr, sm.beta);
+                write_tile<DK, DV, R>(tr, sm.qs, sm.ks, sm.vs);
+                __syncthreads();
+                const float gc = sm.beta[c::C - 1];
+                if (r + 1 < rv) {
+                    load_tile<DK, DV, R>(hr, tpos + kTile, static_cast<uint32_t>(cpos), tr);
+                } else if (ch + 1 < ce) {
+                    load_tile<DK, DV, R>(hr, static_cast<uint32_t>(cpos + c::C),
+                                         static_cast<uint32_t>(cpos + c::C), tr);
                 }
-                // scale output row j by exp(beta_j)
-#pragma unroll
-                for (int jt = 0; jt < 4; ++jt) {
-                    const float f = __expf(sm.beta[kTile * r + 16 * jt + li]);
-#pragma unroll
-                    for (int tc = 0; tc < c::TC; ++tc) {
-                        o[jt][tc][0] *= f;
-                        o[jt][tc][1] *= f;
-                        o[jt][tc][2] *= f;
-                        o[jt][tc][3] *= f;
-                    }
-                }
-                // intra-chunk terms: earlier tiles of this chunk, then the diagonal tile
-                if constexpr (R > 1) {
+                if (full) {
+                    f32x4 o[4];
+                    cross_term<DK, DV, R>(sm, a, r, o);
                     for (int t = 0; t < r; ++t) {
-                        restage<DK, DV, R>(p, x, cpos + kTile * t, *s2);
+                        restage<DK, DV, R>(hr, static_cast<uint32_t>(cpos + kTile * t), *s2);
                         __syncthreads();
                         scores_to_lds<DK, DV, R>(sm, s2->ks, r, t, false);
                         __syncthreads();
-                        apply_scores<DK, DV, R>(sm, s2->vts, false, o);
+                        apply_scores<DK, DV, R>(sm, s2->vs, false, o);
                         __syncthreads();
                     }
+                    scores_to_lds<DK, DV, R>(sm, sm.ks, r, r, true);
+                    __syncthreads();
+                    apply_scores<DK, DV, R>(sm, sm.vs, true, o);
+                    store_out<DK, DV, R>(hr.out, tpos, o);
                 }
-                scores_to_lds<DK, DV, R>(sm, sm.ks, r, r, true);
-                __syncthreads();
-                apply_scores<DK, DV, R>(sm, sm.vts, true, o);
-                store_out<DK, DV, R>(p, x, tpos, o);
-            }
-
-            // state carry
-            if constexpr (R == 1) {
-                const float eg = __expf(gc);
-#pragma unroll
-                for (int tk = 0; tk < c::TK; ++tk)
-#pragma unroll
-                    for (int tc = 0; tc < c::TC; ++tc) {
-                        a.s[tk][tc][0] *= eg;
-                        a.s[tk][tc][1] *= eg;
-                        a.s[tk][tc][2] *= eg;
-                        a.s[tk][tc][3] *= eg;
-                    }
-                state_update<DK, DV, R>(sm, r, gc, a.s);
-            } else {
                 state_update<DK, DV, R>(sm, r, gc, a.ds);
                 if (r == rv - 1) {
                     const float eg = __expf(gc);
 #pragma unroll
-                    for (int tk = 0; tk < c::TK; ++tk)
-#pragma unroll
-                        for (int tc = 0; tc < c::TC; ++tc) {
-                            f32x4& sv = a.s[tk][tc];
-                            f32x4& dv = a.ds[tk][tc];
-                            sv[0] = fmaf(eg, sv[0], dv[0]);
-                            sv[1] = fmaf(eg, sv[1], dv[1]);
-                            sv[2] = fmaf(eg, sv[2], dv[2]);
-                            sv[3] = fmaf(eg, sv[3], dv[3]);
-                            dv = f32x4{0.f, 0.f, 0.f, 0.f};
-                        }
+                    for (int tk = 0; tk < c::TK; ++tk) {
+                        f32x4& sv = a.s[tk];
+                        f32x4& dv = a.ds[tk];
+                        sv[0] = fmaf(eg, sv[0], dv[0]);
+                        sv[1] = fmaf(eg, sv[1], dv[1]);
+                        sv[2] = fmaf(eg, sv[2], dv[2]);
+                        sv[3] = fmaf(eg, sv[3], dv[3]);
+                        dv = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+                    total += gc;
+                    if (!full && total < kSurvivalDropLog) {
+                        full = true;
+                        *lead = ch + 1 - cb;
+                    }
                 }
+                __syncthreads();  // LDS tiles are rewritten next iteration
             }
-            if (r == rv - 1) {
-                total += gc;
-                if (!full && total < kSurvivalDropLog) {
-                    full = true;
-                    *lead = ch + 1 - cb;
-                }
-            }
-            __syncthreads();  // LDS tiles are rewritten next iteration
         }
+        return total;
     }
-    (void)li;
-    (void)g;
-    return total;
 }
 
 template <int DK, int DV, int R>
@@ -535,13 +587,15 @@ __device__ inline void load_state(Acc<DK, DV, R>& a, const float* src) {
     using c = Cfg<DK, DV, R>;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int li = lane & 15, g = lane >> 4;
+    if (!src) {
+#pragma unroll
+        for (int tk = 0; tk < c::TK; ++tk) a.s[tk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        return;
+    }
 #pragma unroll
     for (int tk = 0; tk < c::TK; ++tk)
 #pragma unroll
-        for (int tc = 0; tc < c::TC; ++tc)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a.s[tk][tc][i] = src ? src[(16 * tk + 4 * g + i) * DV + c::CW * w + 16 * tc + li] : 0.0f;
+        for (int i = 0; i < 4; ++i) a.s[tk][i] = src[(16 * tk + 4 * g + i) * DV + 16 * w + li];
 }
 
 template <int DK, int DV, int R>
@@ -552,16 +606,11 @@ __device__ inline void save_state(const Acc<DK, DV, R>& a, float* dst) {
 #pragma unroll
     for (int tk = 0; tk < c::TK; ++tk)
 #pragma unroll
-        for (int tc = 0; tc < c::TC; ++tc)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dst[(16 * tk + 4 * g + i) * DV + c::CW * w + 16 * tc + li] = a.s[tk][tc][i];
+        for (int i = 0; i < 4; ++i) dst[(16 * tk + 4 * g + i) * DV + 16 * w + li] = a.s[tk][i];
 }
 
-// One workgroup per CU: the state tiles, the prefetched tile and the
-// operand fragments need more than the 256 registers a lane gets at two.
 template <int DK, int DV, int R>
-__global__ __launch_bounds__(kThreads, 1) void prefill_main_kernel(Params p) {
+__global__ __launch_bounds__(kThreadsFor<DV>) void prefill_main_kernel(Params p) {
     __shared__ SmemAll<DK, DV, R> all;
     Smem<DK, DV, R>& sm = all.m;
     Smem2<DK, DV>* s2 = all.extra();
@@ -587,7 +636,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_main_kernel(Params p) {
 }
 
 template <int DK, int DV, int R>
-__global__ __launch_bounds__(kThreads, 1) void prefill_prefix_kernel(Params p) {
+__global__ __launch_bounds__(kThreadsFor<DV>) void prefill_prefix_kernel(Params p) {
     __shared__ SmemAll<DK, DV, R> all;
     Smem<DK, DV, R>& sm = all.m;
     Smem2<DK, DV>* s2 = all.extra();
@@ -609,10 +658,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_prefix_kernel(Params p) {
 // Chains the segment maps of each head: S_in(s) = S_end(s-1),
 // S_end(s) = exp(G_s) S_in(s) + S_loc(s). Leaves S_in(s) in slot s and writes
 // the final state.
+constexpr int kCombineThreads = 256;
+
 template <int DK, int DV>
-__global__ __launch_bounds__(kThreads) void prefill_combine_kernel(Params p) {
+__global__ __launch_bounds__(kCombineThreads) void prefill_combine_kernel(Params p) {
     const SegPlan& pl = p.plan;
-    constexpr int PER_BLOCK = kThreads * 4;
+    constexpr int PER_BLOCK = kCombineThreads * 4;
     constexpr int BLOCKS_PER_HEAD = DK * DV / PER_BLOCK;
     const int64_t x = blockIdx.x / BLOCKS_PER_HEAD;
     const int64_t e0 = (blockIdx.x % BLOCKS_PER_HEAD) * PER_BLOCK + threadIdx.x * 4;
@@ -647,13 +698,13 @@ hipError_t launch_rc(const PrefillArgs& a, const SegPlan& plan) {
     p.ws_meta = reinterpret_cast<float2*>(static_cast<char*>(a.workspace) + lay.meta_off);
     p.plan = plan;
     p.N = a.N;
-    const dim3 block(kThreads);
+    const dim3 block(Cfg<DK, DV, R>::NT);
     hipLaunchKernelGGL((prefill_main_kernel<DK, DV, R>), dim3(plan.G), block, 0, a.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int per_head = DK * DV / (kThreads * 4);
-    hipLaunchKernelGGL((prefill_combine_kernel<DK, DV>), dim3(plan.BH * per_head), block, 0,
-                       a.stream, p);
+    const int per_head = DK * DV / (kCombineThreads * 4);
+    hipLaunchKernelGGL((prefill_combine_kernel<DK, DV>), dim3(plan.BH * per_head),
+                       dim3(kCombineThreads), 0, a.stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_prefix_kernel<DK, DV, R>), dim3(plan.G), block, 0, a.stream, p);
@@ -673,8 +724,8 @@ hipError_t launch_dims(const PrefillArgs& a, const SegPlan& plan) {
 template <int DK, int DV, int R>
 int blocks_per_cu_rc() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_main_kernel<DK, DV, R>, kThreads,
-                                                      0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_main_kernel<DK, DV, R>,
+                                                      Cfg<DK, DV, R>::NT, 0) != hipSuccess)
         return 0;
     return n;
 }
