@@ -147,26 +147,48 @@ struct Cfg {
 template <int DV>
 constexpr int kThreadsFor = DV * 4;
 
-// XOR swizzle of the 16-byte chunks of a row-major tile row. Reads of 8
-// consecutive rows at one chunk hit 8 different chunk slots, and the 4 rows x
-// 2 chunks touched by one 16-lane group of a transposing read map to 8
-// different slots, so both access patterns are free of bank conflicts.
-__device__ inline int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+// XOR swizzle of the 16-byte chunks of a row-major tile row. The LDS serves
+// 16 lanes x 16 bytes per cycle, so 16 consecutive rows read at one chunk must
+// land in 16 different chunk slots; and one 16-lane group of a transposing
+// read touches 4 consecutive rows x 2 adjacent chunks (an even chunk and the
+// next), at rows t0..t0+3 and t0+8..t0+11 for the two groups served together.
+// For 16-chunk rows (128 columns) the slot is c ^ (4 (r % 4) + (r / 4) % 4):
+// a bijection on 16 rows, and its bits 1..3 (which decide the 32-byte pair of
+// an even/odd chunk) take 8 different values over each such set of 8 rows.
+// 8-chunk rows (64 columns) use c ^ (2 (r % 4) + (r / 4) % 2).
+template <int D>
+__device__ inline int swz(int row) {
+    if constexpr (D / 8 >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    return 2 * (row & 3) + ((row >> 2) & 1);
+}
 
 // Element offset of (row, col) in a swizzled row-major tile with D columns.
 template <int D>
 __device__ inline int toff(int row, int col) {
-    return row * D + (((col >> 3) ^ swz(row)) << 3) + (col & 7);
+    return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
 }
 
+// One staged tile and the per-chunk tables derived from its log-gates.
 template <int DK, int DV, int R>
-struct __attribute__((aligned(16))) Smem {
+struct __attribute__((aligned(16))) TileBuf {
     using c = Cfg<DK, DV, R>;
     bf16_t qs[kTile * DK];
     bf16_t ks[kTile * DK];
     bf16_t vs[kTile * DV];
+    float beta[c::C];  // chunk-local inclusive log-decay
+    float gam[c::C];   // exp(beta_last - beta_l): weight of position l in the state update
+    float fexp[c::C];  // exp(beta_j): weight of the incoming state in output j
+};
+
+// Chunks of 64 double-buffer the staged tile (the next chunk is written while
+// slower wavefronts still read the current one), which saves a barrier.
+template <int DK, int DV, int R>
+struct __attribute__((aligned(16))) Smem {
+    using c = Cfg<DK, DV, R>;
+    static constexpr int NB = R == 1 ? 2 : 1;
+    TileBuf<DK, DV, R> buf[NB];
     bf16_t ps[kTile * c::PP];
-    float beta[c::C];
+    bf16_t os[R == 1 ? kTile * DV : 8];  // output tile staged for full-row stores
 };
 
 template <int DK, int DV>
@@ -241,10 +263,11 @@ __device__ inline void write_tile(const TileRegs<DK, DV, R>& t, bf16_t* qs, bf16
     }
 }
 
-// Wave 0: chunk-local inclusive prefix sum of the clamped log-gates into
-// beta[C] (positions past the end read as log-gate 0).
+// Wave 0: chunk-local inclusive prefix sum of the clamped log-gates
+// (positions past the end read as log-gate 0) and the two exponential tables
+// of the chunk.
 template <int DK, int DV, int R>
-__device__ inline void scan_beta(const TileRegs<DK, DV, R>& t, float* beta) {
+__device__ inline void make_tables(const TileRegs<DK, DV, R>& t, TileBuf<DK, DV, R>& tb) {
     const int tid = threadIdx.x;
     if (tid >= 64) return;
     float loc[R];
@@ -260,9 +283,15 @@ __device__ inline void scan_beta(const TileRegs<DK, DV, R>& t, float* beta) {
         const float o = __shfl_up(tot, off);
         if (tid >= off) tot += o;
     }
+    const float gc = __shfl(tot, 63);
     const float excl = tot - run;
 #pragma unroll
-    for (int i = 0; i < R; ++i) beta[tid * R + i] = excl + loc[i];
+    for (int i = 0; i < R; ++i) {
+        const float b = excl + loc[i];
+        tb.beta[tid * R + i] = b;
+        tb.gam[tid * R + i] = __expf(gc - b);
+        tb.fexp[tid * R + i] = __expf(b);
+    }
 }
 
 // 8 consecutive positions t0..t0+7 of column col0 + l (l = this lane's index
@@ -298,8 +327,8 @@ __device__ inline void restage(const HeadRsrc& hr, uint32_t pos, Smem2<DK, DV>& 
 // by exp(beta_j). The state tile pair (2m, 2m+1) gives each lane
 // dk = 32m + {4g..4g+3, 16+4g..16+4g+3}; the Q operand is read with the same
 // permutation of dk, so the contraction pairs matching indices.
-template <int DK, int DV, int R>
-__device__ inline void cross_term(const Smem<DK, DV, R>& sm, const Acc<DK, DV, R>& a, int r,
+template <int DK, int DV, int R, class TB>
+__device__ inline void cross_term(const TB& tb, const Acc<DK, DV, R>& a, int r,
                                   f32x4 (&o)[4]) {
     using c = Cfg<DK, DV, R>;
     const int lane = threadIdx.x & 63;
@@ -314,14 +343,14 @@ __device__ inline void cross_term(const Smem<DK, DV, R>& sm, const Acc<DK, DV, R
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             const int row = 16 * jt + li;
-            const bf16x8 qf = cat44(lds_read4(sm.qs + toff<DK>(row, 32 * m + 4 * g)),
-                                    lds_read4(sm.qs + toff<DK>(row, 32 * m + 16 + 4 * g)));
+            const bf16x8 qf = cat44(lds_read4(tb.qs + toff<DK>(row, 32 * m + 4 * g)),
+                                    lds_read4(tb.qs + toff<DK>(row, 32 * m + 16 + 4 * g)));
             o[jt] = mfma16(sf, qf, o[jt]);
         }
     }
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
-        const float f = __expf(sm.beta[kTile * r + 16 * jt + li]);
+        const float f = tb.fexp[kTile * r + 16 * jt + li];
         o[jt][0] *= f;
         o[jt][1] *= f;
         o[jt][2] *= f;
@@ -329,51 +358,80 @@ __device__ inline void cross_term(const Smem<DK, DV, R>& sm, const Acc<DK, DV, R
     }
 }
 
-// Decayed scores of query tile r against key tile t of the chunk, written as
-// bf16 to sm.ps[j][l]. Wave w computes the 16x16 blocks (jb, b) with
-// jb = w / BSTEP and b = w % BSTEP, w % BSTEP + BSTEP, ...; blocks above the
-// diagonal (diag only) are written as zeros.
-template <int DK, int DV, int R>
-__device__ inline void scores_to_lds(Smem<DK, DV, R>& sm, const bf16_t* ksrc, int r, int t,
-                                     bool diag) {
+// Decayed score block (jb, b): rows 16jb.. of query tile r against columns
+// 16b.. of key tile t, written as bf16 to ps[j][l]. With diag, entries above
+// the diagonal are zero.
+template <int DK, int DV, int R, class TB>
+__device__ inline void score_block(const TB& tb, bf16_t* ps, const bf16_t* ksrc,
+                                   int r, int t, int jb, int b, bool diag) {
     using c = Cfg<DK, DV, R>;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
-    const int jb = w / c::BSTEP;
     const int jrow = 16 * jb + li;
-    const float bj = sm.beta[kTile * r + jrow];
-    bf16x8 qf[c::KS];
+    const float bj = tb.beta[kTile * r + jrow];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < c::KS; ++ks) qf[ks] = lds_read8(sm.qs + toff<DK>(jrow, 32 * ks + 8 * g));
+    for (int ks = 0; ks < c::KS; ++ks) {
+        const bf16x8 qf = lds_read8(tb.qs + toff<DK>(jrow, 32 * ks + 8 * g));
+        const bf16x8 kf = lds_read8(ksrc + toff<DK>(16 * b + li, 32 * ks + 8 * g));
+        acc = mfma16(kf, qf, acc);
+    }
+    // acc[i] = P^T[l = 16b + 4g + i][j = jrow]
+    bf16x4 pk;
 #pragma unroll
-    for (int b0 = 0; b0 < 4; b0 += c::BSTEP) {
-        const int b = b0 + w % c::BSTEP;
-        bf16x4 pk;
-        if (!diag || b <= jb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < c::KS; ++ks) {
-                const bf16x8 kf = lds_read8(ksrc + toff<DK>(16 * b + li, 32 * ks + 8 * g));
-                acc = mfma16(kf, qf[ks], acc);
-            }
-            // acc[i] = P^T[l = 16b + 4g + i][j = jrow]
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int l = 16 * b + 4 * g + i;
-                float val = 0.0f;
-                if (!diag || l <= jrow) val = acc[i] * __expf(bj - sm.beta[kTile * t + l]);
-                pk[i] = to_bf16(val);
-            }
-        } else {
-            pk = bf16x4{};
-        }
-        *reinterpret_cast<bf16x4*>(sm.ps + jrow * c::PP + 16 * b + 4 * g) = pk;
+    for (int i = 0; i < 4; ++i) {
+        const int l = 16 * b + 4 * g + i;
+        float val = 0.0f;
+        if (!diag || l <= jrow) val = acc[i] * __expf(bj - tb.beta[kTile * t + l]);
+        pk[i] = to_bf16(val);
+    }
+    *reinterpret_cast<bf16x4*>(ps + jrow * c::PP + 16 * b + 4 * g) = pk;
+}
+
+// The 10 blocks on or below the diagonal of a 64x64 score tile, largest rows
+// first: (3,3) (3,2) (2,2) (3,1) (2,1) (1,1) (3,0) (2,0) (1,0) (0,0), packed as
+// 4-bit (4 jb + b) entries of an immediate (a table in memory would be a
+// global load that the compiler waits for together with the prefetches).
+constexpr uint64_t kCausalBlocks = 0xFull | 0xEull << 4 | 0xAull << 8 | 0xDull << 12 |
+                                   0x9ull << 16 | 0x5ull << 20 | 0xCull << 24 | 0x8ull << 28 |
+                                   0x4ull << 32 | 0x0ull << 36;
+
+// Wave w computes entries w, w + NW, ...
+template <int DK, int DV, int R, class TB>
+__device__ inline void scores_diag(const TB& tb, bf16_t* ps, int r) {
+    using c = Cfg<DK, DV, R>;
+    const int w = threadIdx.x >> 6;
+    for (int i = w; i < 10; i += c::NW) {
+        const int e = static_cast<int>((kCausalBlocks >> (4 * i)) & 0xF);
+        score_block<DK, DV, R>(tb, ps, tb.ks, r, r, e >> 2, e & 3, true);
+    }
+}
+
+template <int DK, int DV, int R, class TB>
+__device__ inline void scores_full(const TB& tb, bf16_t* ps, const bf16_t* ksrc,
+                                   int r, int t) {
+    using c = Cfg<DK, DV, R>;
+    const int w = threadIdx.x >> 6;
+    for (int i = w; i < 16; i += c::NW)
+        score_block<DK, DV, R>(tb, ps, ksrc, r, t, i >> 2, i & 3, false);
+}
+
+// Blocks (0,1) and (2,3) lie above the diagonal but inside 32-position steps
+// that the diagonal product uses; they hold zeros.
+template <int DK, int DV, int R>
+__device__ inline void zero_upper_blocks(bf16_t* ps) {
+    using c = Cfg<DK, DV, R>;
+    for (int e = threadIdx.x; e < 2 * 16 * 4; e += c::NT) {
+        const int blk = e / 64, rem = e % 64;
+        const int jb = blk == 0 ? 0 : 2, b = jb + 1;
+        const int row = 16 * jb + rem / 4, col = 16 * b + 4 * (rem % 4);
+        *reinterpret_cast<bf16x4*>(ps + row * c::PP + col) = bf16x4{};
     }
 }
 
 // O^T[cols][rows] += V_t^T P~^T over the positions of tile t (V read transposed).
 template <int DK, int DV, int R>
-__device__ inline void apply_scores(const Smem<DK, DV, R>& sm, const bf16_t* vsrc, bool diag,
+__device__ inline void apply_scores(const bf16_t* ps, const bf16_t* vsrc, bool diag,
                                     f32x4 (&o)[4]) {
     using c = Cfg<DK, DV, R>;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -384,7 +442,7 @@ __device__ inline void apply_scores(const Smem<DK, DV, R>& sm, const bf16_t* vsr
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             if (diag && 2 * ks > jt) continue;  // whole 32-position step is above the diagonal
-            const bf16x8 pf = lds_read8(sm.ps + (16 * jt + li) * c::PP + 32 * ks + 8 * g);
+            const bf16x8 pf = lds_read8(ps + (16 * jt + li) * c::PP + 32 * ks + 8 * g);
             o[jt] = mfma16(vf, pf, o[jt]);
         }
     }
@@ -404,10 +462,42 @@ __device__ inline void store_out(const __amdgpu_buffer_rsrc_t& out, uint32_t til
     }
 }
 
-// acc += K^T (Gamma V) over the current tile, Gamma_l = exp(gc - beta_l); K and
-// V are read transposed so that positions are the contraction index.
+// Output through LDS: each lane's fragment (4 consecutive columns of one row)
+// goes to a swizzled row-major tile, and whole rows then leave with 16-byte
+// stores, so every store instruction of a wavefront covers 4 complete 256-byte
+// rows instead of sixteen 32-byte pieces.
 template <int DK, int DV, int R>
-__device__ inline void state_update(const Smem<DK, DV, R>& sm, int r, float gc,
+__device__ inline void out_to_lds(bf16_t* os, const f32x4 (&o)[4]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int li = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+        const bf16x4 pk = {to_bf16(o[jt][0]), to_bf16(o[jt][1]), to_bf16(o[jt][2]),
+                           to_bf16(o[jt][3])};
+        *reinterpret_cast<bf16x4*>(os + toff<DV>(16 * jt + li, 16 * w + 4 * g)) = pk;
+    }
+}
+
+template <int DK, int DV, int R>
+__device__ inline void flush_out(const bf16_t* os, const __amdgpu_buffer_rsrc_t& out,
+                                 uint32_t tile_pos) {
+    using c = Cfg<DK, DV, R>;
+    constexpr int PER = kTile * c::VCH / c::NT;  // 16-byte pieces per thread
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int id = threadIdx.x + i * c::NT;
+        const int row = id / c::VCH, ch = id % c::VCH;
+        const bf16x8 v = lds_read8(os + toff<DV>(row, 8 * ch));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), out,
+                                               ((tile_pos + row) * DV + 8 * ch) * 2, 0, 0);
+    }
+}
+
+// acc += K^T (Gamma V) over tile r of the chunk, Gamma_l = exp(g - beta_l)
+// from the chunk table; K and V are read transposed so that positions are the
+// contraction index.
+template <int DK, int DV, int R, class TB>
+__device__ inline void state_update(const TB& tb, int r,
                                     f32x4 (&acc)[Cfg<DK, DV, R>::TK]) {
     using c = Cfg<DK, DV, R>;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -415,14 +505,16 @@ __device__ inline void state_update(const Smem<DK, DV, R>& sm, int r, float gc,
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const int t0 = 32 * ks + 8 * g;
-        const bf16x8 vf = read_cols8<DV>(sm.vs, t0, 16 * w);
-        bf16x8 bf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            bf[e] = to_bf16(from_bf16(vf[e]) * __expf(gc - sm.beta[kTile * r + t0 + e]));
+        const bf16x8 vf = read_cols8<DV>(tb.vs, t0, 16 * w);
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(tb.gam + kTile * r + t0);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(tb.gam + kTile * r + t0 + 4);
+        const bf16x8 bf = {to_bf16(from_bf16(vf[0]) * g0[0]), to_bf16(from_bf16(vf[1]) * g0[1]),
+                           to_bf16(from_bf16(vf[2]) * g0[2]), to_bf16(from_bf16(vf[3]) * g0[3]),
+                           to_bf16(from_bf16(vf[4]) * g1[0]), to_bf16(from_bf16(vf[5]) * g1[1]),
+                           to_bf16(from_bf16(vf[6]) * g1[2]), to_bf16(from_bf16(vf[7]) * g1[3])};
 #pragma unroll
         for (int tk = 0; tk < c::TK; ++tk) {
-            const bf16x8 kf = read_cols8<DK>(sm.ks, t0, 16 * tk);
+            const bf16x8 kf = read_cols8<DK>(tb.ks, t0, 16 * tk);
             acc[tk] = mfma16(kf, bf, acc[tk]);
         }
     }
@@ -452,13 +544,43 @@ __device__ inline void scale_state(Acc<DK, DV, R>& a, float eg) {
     }
 }
 
+// One chunk of 64 positions from the staged buffer `cur`. It first stores the
+// previous chunk's output tile (staged in LDS, `prev_out` / `prev_pos`), then
+// computes this chunk, leaves its output tile in LDS, stages the next chunk
+// (already in `stage`) into the other buffer and refills `stage` with the chunk
+// three ahead. Returns the chunk's total log-decay.
+template <int DK, int DV, int R>
+__device__ inline float chunk_c64(const HeadRsrc& hr, const __amdgpu_buffer_rsrc_t& prev_out,
+                                  uint32_t prev_pos, Smem<DK, DV, R>& sm, int cur, uint32_t pos,
+                                  Acc<DK, DV, R>& a, TileRegs<DK, DV, R>& stage) {
+    const TileBuf<DK, DV, R>& tb = sm.buf[cur];
+    flush_out<DK, DV, R>(sm.os, prev_out, prev_pos);
+    f32x4 o[4];
+    cross_term<DK, DV, R>(tb, a, 0, o);
+    scores_diag<DK, DV, R>(tb, sm.ps, 0);
+    __syncthreads();
+    apply_scores<DK, DV, R>(sm.ps, tb.vs, true, o);
+    out_to_lds<DK, DV, R>(sm.os, o);
+    const float gc = tb.beta[kTile - 1];
+    scale_state<DK, DV, R>(a, __expf(gc));
+    state_update<DK, DV, R>(tb, 0, a.s);
+    TileBuf<DK, DV, R>& nb = sm.buf[cur ^ 1];
+    make_tables<DK, DV, R>(stage, nb);
+    write_tile<DK, DV, R>(stage, nb.qs, nb.ks, nb.vs);
+    load_tile<DK, DV, R>(hr, pos + 3 * kTile, pos + 3 * kTile, stage);
+    __syncthreads();
+    return gc;
+}
+
 // Chunks of 64 positions (one tile per chunk): a branch-free steady-state
-// loop. The next chunk is always prefetched (reads past the head's end return
-// zeros), and in state-only mode the outputs are still computed but stored
+// loop over double-buffered LDS tiles with two barriers per chunk, fed by two
+// register sets so that every tile's loads are issued two chunks before they
+// are staged (about 100 KB in flight per CU). Reads past the head's end return
+// zeros, and in state-only mode the outputs are still computed but stored
 // through a zero-length descriptor, so the hardware drops them. Every
 // iteration therefore issues the same memory operations in the same order,
-// which lets the compiler wait only for the prefetched loads at the top of the
-// loop while the previous chunk's output stores are still in flight.
+// which lets the compiler wait only for the loads it stages while younger
+// loads and the output stores stay in flight.
 template <int DK, int DV, int R>
 __device__ float run_chunks_c64(const Params& p, Smem<DK, DV, R>& sm, int64_t x, int64_t cb,
                                 int64_t ce, bool full_from_start, Acc<DK, DV, R>& a,
@@ -469,38 +591,285 @@ __device__ float run_chunks_c64(const Params& p, Smem<DK, DV, R>& sm, int64_t x,
     *lead = full ? 0 : (ce - cb);
     const HeadRsrc hr = head_rsrc<DK, DV, R>(p, x);
     const __amdgpu_buffer_rsrc_t drop = make_rsrc(p.out, 0);
-    TileRegs<DK, DV, R> tr;
+    TileRegs<DK, DV, R> ta, tb;
     uint32_t pos = static_cast<uint32_t>(cb * kTile);
-    load_tile<DK, DV, R>(hr, pos, pos, tr);
-    {
-        const f32x4 z[4] = {};
-        store_out<DK, DV, R>(drop, 0, z);  // same store pattern as the loop, all dropped
-    }
-    for (int64_t ch = cb; ch < ce; ++ch, pos += kTile) {
-        scan_beta<DK, DV, R>(tr, sm.beta);
-        write_tile<DK, DV, R>(tr, sm.qs, sm.ks, sm.vs);
-        __syncthreads();
-        const float gc = sm.beta[kTile - 1];
-        load_tile<DK, DV, R>(hr, pos + kTile, pos + kTile, tr);
-
-        f32x4 o[4];
-        cross_term<DK, DV, R>(sm, a, 0, o);
-        scores_to_lds<DK, DV, R>(sm, sm.ks, 0, 0, true);
-        __syncthreads();
-        apply_scores<DK, DV, R>(sm, sm.vs, true, o);
-        store_out<DK, DV, R>(full ? hr.out : drop, pos, o);
-
-        scale_state<DK, DV, R>(a, __expf(gc));
-        state_update<DK, DV, R>(sm, 0, gc, a.s);
+    load_tile<DK, DV, R>(hr, pos, pos, ta);
+    load_tile<DK, DV, R>(hr, pos + kTile, pos + kTile, tb);
+    __syncthreads();  // the previous segment of this workgroup is done with the LDS tiles
+    flush_out<DK, DV, R>(sm.os, drop, 0);  // same store pattern as the loop, all dropped
+    make_tables<DK, DV, R>(ta, sm.buf[0]);
+    write_tile<DK, DV, R>(ta, sm.buf[0].qs, sm.buf[0].ks, sm.buf[0].vs);
+    load_tile<DK, DV, R>(hr, pos + 2 * kTile, pos + 2 * kTile, ta);
+    __syncthreads();
+    __amdgpu_buffer_rsrc_t prev_out = drop;
+    uint32_t prev_pos = 0;
+    for (int64_t ch = cb; ch < ce; ch += 2, pos += 2 * kTile) {
+        float gc = chunk_c64<DK, DV, R>(hr, prev_out, prev_pos, sm, 0, pos, a, tb);
+        prev_out = full ? hr.out : drop;
+        prev_pos = pos;
         total += gc;
         if (!full && total < kSurvivalDropLog) {
             full = true;
             *lead = ch + 1 - cb;
         }
-        __syncthreads();  // LDS tiles are rewritten next iteration
+        if (ch + 1 >= ce) break;
+        gc = chunk_c64<DK, DV, R>(hr, prev_out, prev_pos, sm, 1, pos + kTile, a, ta);
+        prev_out = full ? hr.out : drop;
+        prev_pos = pos + kTile;
+        total += gc;
+        if (!full && total < kSurvivalDropLog) {
+            full = true;
+            *lead = ch + 2 - cb;
+        }
     }
+    flush_out<DK, DV, R>(sm.os, prev_out, prev_pos);  // the last chunk's output tile
     return total;
 }
+
+// ---------------------------------------------------------------------------
+// Chunk-64 path fed by LDS DMA.
+//
+// Tiles go from HBM straight into LDS with buffer_load ... lds (no registers
+// involved), into three buffer sets, so that while chunk n is computed the
+// tiles of chunks n+1 and n+2 are in flight. The compiler tracks LDS DMA per
+// LDS object, so each set is a distinct __shared__ array and the loop is
+// unrolled by three to keep every access's target set a compile-time fact.
+// Publication of a tile to the other wavefronts is explicit: each wavefront
+// waits for its own DMA writes of that tile (s_waitcnt vmcnt with the number
+// of its younger memory operations, which the loop keeps constant), then all
+// meet at a barrier. Barriers here carry no release fence, so they do not
+// drain the loads still in flight for the next tiles.
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct TileView {
+    const bf16_t* qs;
+    const bf16_t* ks;
+    const bf16_t* vs;
+    const float* beta;
+    const float* gam;
+    const float* fexp;
+};
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wavefront are outstanding (gfx9 encoding; expcnt and lgkmcnt left alone).
+constexpr int vm_wait_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kLgkmWaitZero = 0xC07F;  // lgkmcnt(0) only
+
+template <int N>
+__device__ inline void wait_vm() {
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(N));
+}
+
+// Workgroup barrier for LDS data: this wavefront's LDS writes complete, then
+// s_barrier; compiler-only fences keep memory accesses on their side.
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(kLgkmWaitZero);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One 1 KB DMA instruction of a swizzled row-major tile with D columns: lane i
+// lands at LDS byte 16 i of block blk, i.e. row (512/D) blk + i / (D/8), slot
+// i % (D/8), so it fetches the global 16-byte chunk slot ^ swz(row) of that row.
+template <int D>
+__device__ inline void dma_block(__amdgpu_buffer_rsrc_t r, bf16_t* tile, int blk,
+                                 uint32_t tile_pos) {
+    constexpr int RPI = 512 / D;  // rows per instruction
+    constexpr int SPR = D / 8;    // 16-byte slots per row
+    const int lane = threadIdx.x & 63;
+    const int row = RPI * blk + lane / SPR;
+    const int chunk = (lane % SPR) ^ swz<D>(row);
+    const uint32_t voff = ((tile_pos + row) * D + chunk * 8) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + blk * 512), 16, voff, 0, 0, 0);
+}
+
+template <int DK, int DV>
+struct C64Lds {
+    bf16_t* q[3];
+    bf16_t* k[3];
+    bf16_t* v[3];
+    float* ell[3];
+    float* tab[3];  // beta[64] | gam[64] | fexp[64]
+    bf16_t* ps;
+};
+
+template <int DK, int DV>
+struct C64Counts {
+    static constexpr int NW = DV / 16;
+    static constexpr int QB = DK / 8 / NW;  // DMA blocks of Q (and of K) per wavefront
+    static constexpr int VB = DV / 8 / NW;  // DMA blocks of V per wavefront
+    static constexpr int DMA = 2 * QB + VB; // per wavefront and tile (+1 log-gate DMA on wave 0)
+    static constexpr int ST = 4;            // output stores per wavefront and chunk
+    static_assert(QB * NW * 8 == DK && VB * NW * 8 == DV, "DMA split");
+};
+
+// Issues this wavefront's share of the DMA of the tile at tile_pos into set X.
+template <int DK, int DV, int X>
+__device__ inline void dma_tile(const C64Lds<DK, DV>& L, const HeadRsrc& hr, uint32_t tile_pos) {
+    using n = C64Counts<DK, DV>;
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < n::QB; ++i) dma_block<DK>(hr.q, L.q[X], w * n::QB + i, tile_pos);
+#pragma unroll
+    for (int i = 0; i < n::QB; ++i) dma_block<DK>(hr.k, L.k[X], w * n::QB + i, tile_pos);
+#pragma unroll
+    for (int i = 0; i < n::VB; ++i) dma_block<DV>(hr.v, L.v[X], w * n::VB + i, tile_pos);
+    if (w == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hr.lg, (lds_void*)L.ell[X], 4,
+                                                 (tile_pos + (threadIdx.x & 63)) * 4, 0, 0, 0);
+}
+
+// Waits until this wavefront's DMA writes of the tile used by the k-th chunk of
+// the pass are complete. Younger operations of the wavefront: the next tile's
+// DMA (from chunk k-1) and the output stores of chunks k-2 and k-1.
+template <int DK, int DV>
+__device__ inline void wait_tile(int k) {
+    using n = C64Counts<DK, DV>;
+    const bool w0 = threadIdx.x < 64;
+    if (k == 0) {
+        if (w0) wait_vm<n::DMA + 1>(); else wait_vm<n::DMA>();
+    } else if (k == 1) {
+        if (w0) wait_vm<n::DMA + 1 + n::ST>(); else wait_vm<n::DMA + n::ST>();
+    } else {
+        if (w0) wait_vm<n::DMA + 1 + 2 * n::ST>(); else wait_vm<n::DMA + 2 * n::ST>();
+    }
+}
+
+// Wave 0: chunk tables from the DMA'd log-gates (past the end they read 0).
+__device__ inline void tables_from_lds(const float* ell, float* tab) {
+    const int lane = threadIdx.x;
+    float b = clamp_log_gamma(ell[lane], kLogGammaFloor);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(b, off);
+        if (lane >= off) b += o;
+    }
+    const float gc = __shfl(b, 63);
+    tab[lane] = b;
+    tab[64 + lane] = __expf(gc - b);
+    tab[128 + lane] = __expf(b);
+}
+
+template <int DK, int DV, int X>
+__device__ inline float chunk_dma(const C64Lds<DK, DV>& L, const HeadRsrc& hr,
+                                  const __amdgpu_buffer_rsrc_t& out, int k, uint32_t pos,
+                                  Acc<DK, DV, 1>& a) {
+    wait_tile<DK, DV>(k);
+    if (threadIdx.x < 64) tables_from_lds(L.ell[X], L.tab[X]);
+    lds_barrier();
+    dma_tile<DK, DV, (X + 2) % 3>(L, hr, pos + 2 * kTile);
+    const TileView tv{L.q[X], L.k[X], L.v[X], L.tab[X], L.tab[X] + 64, L.tab[X] + 128};
+    f32x4 o[4];
+    cross_term<DK, DV, 1>(tv, a, 0, o);
+    scores_diag<DK, DV, 1>(tv, L.ps, 0);
+    lds_barrier();
+    apply_scores<DK, DV, 1>(L.ps, tv.vs, true, o);
+    store_out<DK, DV, 1>(out, pos, o);
+    const float gc = tv.beta[kTile - 1];
+    scale_state<DK, DV, 1>(a, __expf(gc));
+    state_update<DK, DV, 1>(tv, 0, a.s);
+    return gc;
+}
+
+// Runs chunks [cb, ce) of head x through the DMA pipeline (same contract as
+// run_chunks).
+template <int DK, int DV>
+__device__ float run_chunks_dma(const Params& p, const C64Lds<DK, DV>& L, int64_t x, int64_t cb,
+                                int64_t ce, bool full_from_start, Acc<DK, DV, 1>& a,
+                                int64_t* lead) {
+    bool full = full_from_start;
+    float total = 0.0f;
+    *lead = full ? 0 : (ce - cb);
+    const HeadRsrc hr = head_rsrc<DK, DV, 1>(p, x);
+    const __amdgpu_buffer_rsrc_t drop = make_rsrc(p.out, 0);
+    const int nch = static_cast<int>(ce - cb);
+    uint32_t pos = static_cast<uint32_t>(cb * kTile);
+    // earlier passes of this workgroup: drain their DMA, and let every
+    // wavefront finish reading the buffers
+    wait_vm<0>();
+    lds_barrier();
+    dma_tile<DK, DV, 0>(L, hr, pos);
+    dma_tile<DK, DV, 1>(L, hr, pos + kTile);
+    auto account = [&](float gc, int k) {
+        total += gc;
+        if (!full && total < kSurvivalDropLog) {
+            full = true;
+            *lead = k + 1;
+        }
+    };
+    for (int k = 0;; k += 3, pos += 3 * kTile) {
+        if (k >= nch) break;
+        account(chunk_dma<DK, DV, 0>(L, hr, full ? hr.out : drop, k, pos, a), k);
+        if (k + 1 >= nch) break;
+        account(chunk_dma<DK, DV, 1>(L, hr, full ? hr.out : drop, k + 1, pos + kTile, a), k + 1);
+        if (k + 2 >= nch) break;
+        account(chunk_dma<DK, DV, 2>(L, hr, full ? hr.out : drop, k + 2, pos + 2 * kTile, a), k + 2);
+    }
+    wait_vm<0>();  // no DMA into this workgroup's LDS may outlive the pass
+    return total;
+}
+
+// LDS of the chunk-64 kernels: three buffer sets, each array its own object.
+#define GRET_C64_LDS(DK, DV)                                                              \
+    __shared__ __attribute__((aligned(16))) bf16_t q0_[kTile * DK], q1_[kTile * DK],      \
+        q2_[kTile * DK];                                                                  \
+    __shared__ __attribute__((aligned(16))) bf16_t k0_[kTile * DK], k1_[kTile * DK],      \
+        k2_[kTile * DK];                                                                  \
+    __shared__ __attribute__((aligned(16))) bf16_t v0_[kTile * DV], v1_[kTile * DV],      \
+        v2_[kTile * DV];                                                                  \
+    __shared__ __attribute__((aligned(16))) float l0_[kTile], l1_[kTile], l2_[kTile];    \
+    __shared__ __attribute__((aligned(16))) float t0_[3 * kTile], t1_[3 * kTile],        \
+        t2_[3 * kTile];                                                                   \
+    __shared__ __attribute__((aligned(16))) bf16_t ps_[kTile * (kTile + kPadP)];          \
+    const C64Lds<DK, DV> L{{q0_, q1_, q2_}, {k0_, k1_, k2_}, {v0_, v1_, v2_},             \
+                           {l0_, l1_, l2_}, {t0_, t1_, t2_}, ps_};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreadsFor<DV>) void prefill_main_c64_kernel(Params p) {
+    GRET_C64_LDS(DK, DV)
+    zero_upper_blocks<DK, DV, 1>(L.ps);  // never rewritten
+    const SegPlan& pl = p.plan;
+    const int64_t gidx = blockIdx.x;
+    const int64_t hi = seg_lo(pl, gidx + 1);
+    int64_t t = seg_lo(pl, gidx);
+    Acc<DK, DV, 1> a;
+    while (t < hi) {
+        const int64_t x = t / pl.nc;
+        const int64_t cb = t - x * pl.nc;
+        const int64_t ce = (hi - x * pl.nc) < pl.nc ? (hi - x * pl.nc) : pl.nc;
+        const bool initial = cb == 0;
+        const int64_t slot = initial ? 0 : gidx - seg_first_inner(pl, x) + 1;
+        load_state<DK, DV, 1>(a, initial && p.state_in ? p.state_in + x * DK * DV : nullptr);
+        int64_t lead = 0;
+        const float total = run_chunks_dma<DK, DV>(p, L, x, cb, ce, initial, a, &lead);
+        float* dst = p.ws_state + (x * pl.max_seg + slot) * (int64_t)(DK * DV);
+        save_state<DK, DV, 1>(a, dst);
+        if (threadIdx.x == 0) p.ws_meta[x * pl.max_seg + slot] = make_float2(total, (float)lead);
+        t = x * pl.nc + ce;
+    }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreadsFor<DV>) void prefill_prefix_c64_kernel(Params p) {
+    GRET_C64_LDS(DK, DV)
+    const SegPlan& pl = p.plan;
+    const int64_t gidx = blockIdx.x;
+    const int64_t lo = seg_lo(pl, gidx);
+    const int64_t x = lo / pl.nc;
+    const int64_t cb = lo - x * pl.nc;
+    if (cb == 0) return;  // this workgroup starts at a head boundary: nothing to redo
+    const int64_t slot = gidx - seg_first_inner(pl, x) + 1;
+    const int64_t lead = static_cast<int64_t>(p.ws_meta[x * pl.max_seg + slot].y);
+    if (lead <= 0) return;
+    zero_upper_blocks<DK, DV, 1>(L.ps);
+    Acc<DK, DV, 1> a;
+    load_state<DK, DV, 1>(a, p.ws_state + (x * pl.max_seg + slot) * (int64_t)(DK * DV));
+    int64_t unused = 0;
+    run_chunks_dma<DK, DV>(p, L, x, cb, cb + lead, true, a, &unused);
+}
+#undef GRET_C64_LDS
 
 // Runs chunks [cb, ce) of head x. With full_from_start the pass computes
 // outputs from the first chunk; otherwise only the state until the running
@@ -530,10 +899,11 @@ __device__ float run_chunks(const Params& p, Smem<DK, DV, R>& sm, Smem2<DK, DV>*
             const int rv = static_cast<int>((nvalid + kTile - 1) / kTile);
             for (int r = 0; r < rv; ++r) {
                 const uint32_t tpos = static_cast<uint32_t>(cpos + kTile * r);
-                if (r == 0) scan_beta<DK, DV, R>(tr, sm.beta);
-                write_tile<DK, DV, R>(tr, sm.qs, sm.ks, sm.vs);
+                TileBuf<DK, DV, R>& tb = sm.buf[0];
+                if (r == 0) make_tables<DK, DV, R>(tr, tb);
+                write_tile<DK, DV, R>(tr, tb.qs, tb.ks, tb.vs);
                 __syncthreads();
-                const float gc = sm.beta[c::C - 1];
+                const float gc = tb.beta[c::C - 1];
                 if (r + 1 < rv) {
                     load_tile<DK, DV, R>(hr, tpos + kTile, static_cast<uint32_t>(cpos), tr);
                 } else if (ch + 1 < ce) {
@@ -542,21 +912,22 @@ __device__ float run_chunks(const Params& p, Smem<DK, DV, R>& sm, Smem2<DK, DV>*
                 }
                 if (full) {
                     f32x4 o[4];
-                    cross_term<DK, DV, R>(sm, a, r, o);
+                    cross_term<DK, DV, R>(tb, a, r, o);
                     for (int t = 0; t < r; ++t) {
                         restage<DK, DV, R>(hr, static_cast<uint32_t>(cpos + kTile * t), *s2);
                         __syncthreads();
-                        scores_to_lds<DK, DV, R>(sm, s2->ks, r, t, false);
+                        scores_full<DK, DV, R>(tb, sm.ps, s2->ks, r, t);
                         __syncthreads();
-                        apply_scores<DK, DV, R>(sm, s2->vs, false, o);
+                        apply_scores<DK, DV, R>(sm.ps, s2->vs, false, o);
                         __syncthreads();
                     }
-                    scores_to_lds<DK, DV, R>(sm, sm.ks, r, r, true);
+                    zero_upper_blocks<DK, DV, R>(sm.ps);
+                    scores_diag<DK, DV, R>(tb, sm.ps, r);
                     __syncthreads();
-                    apply_scores<DK, DV, R>(sm, sm.vs, true, o);
+                    apply_scores<DK, DV, R>(sm.ps, tb.vs, true, o);
                     store_out<DK, DV, R>(hr.out, tpos, o);
                 }
-                state_update<DK, DV, R>(sm, r, gc, a.ds);
+                state_update<DK, DV, R>(tb, r, a.ds);
                 if (r == rv - 1) {
                     const float eg = __expf(gc);
 #pragma unroll
@@ -614,6 +985,7 @@ __global__ __launch_bounds__(kThreadsFor<DV>) void prefill_main_kernel(Params p)
     __shared__ SmemAll<DK, DV, R> all;
     Smem<DK, DV, R>& sm = all.m;
     Smem2<DK, DV>* s2 = all.extra();
+    if constexpr (R == 1) zero_upper_blocks<DK, DV, R>(sm.ps);  // never rewritten
     const SegPlan& pl = p.plan;
     const int64_t gidx = blockIdx.x;
     const int64_t hi = seg_lo(pl, gidx + 1);
@@ -649,6 +1021,7 @@ __global__ __launch_bounds__(kThreadsFor<DV>) void prefill_prefix_kernel(Params 
     const int64_t slot = gidx - seg_first_inner(pl, x) + 1;
     const int64_t lead = static_cast<int64_t>(p.ws_meta[x * pl.max_seg + slot].y);
     if (lead <= 0) return;
+    if constexpr (R == 1) zero_upper_blocks<DK, DV, R>(sm.ps);  // never rewritten
     Acc<DK, DV, R> a;
     load_state<DK, DV, R>(a, p.ws_state + (x * pl.max_seg + slot) * (int64_t)(DK * DV));
     int64_t unused = 0;
@@ -699,7 +1072,10 @@ hipError_t launch_rc(const PrefillArgs& a, const SegPlan& plan) {
     p.plan = plan;
     p.N = a.N;
     const dim3 block(Cfg<DK, DV, R>::NT);
-    hipLaunchKernelGGL((prefill_main_kernel<DK, DV, R>), dim3(plan.G), block, 0, a.stream, p);
+    if constexpr (R == 1)
+        hipLaunchKernelGGL((prefill_main_c64_kernel<DK, DV>), dim3(plan.G), block, 0, a.stream, p);
+    else
+        hipLaunchKernelGGL((prefill_main_kernel<DK, DV, R>), dim3(plan.G), block, 0, a.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int per_head = DK * DV / (kCombineThreads * 4);
@@ -707,7 +1083,10 @@ hipError_t launch_rc(const PrefillArgs& a, const SegPlan& plan) {
                        dim3(kCombineThreads), 0, a.stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_prefix_kernel<DK, DV, R>), dim3(plan.G), block, 0, a.stream, p);
+    if constexpr (R == 1)
+        hipLaunchKernelGGL((prefill_prefix_c64_kernel<DK, DV>), dim3(plan.G), block, 0, a.stream, p);
+    else
+        hipLaunchKernelGGL((prefill_prefix_kernel<DK, DV, R>), dim3(plan.G), block, 0, a.stream, p);
     return hipGetLastError();
 }
 
@@ -724,10 +1103,14 @@ hipError_t launch_dims(const PrefillArgs& a, const SegPlan& plan) {
 template <int DK, int DV, int R>
 int blocks_per_cu_rc() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_main_kernel<DK, DV, R>,
-                                                      Cfg<DK, DV, R>::NT, 0) != hipSuccess)
-        return 0;
-    return n;
+    hipError_t e;
+    if constexpr (R == 1)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_main_c64_kernel<DK, DV>,
+                                                         Cfg<DK, DV, R>::NT, 0);
+    else
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_main_kernel<DK, DV, R>,
+                                                         Cfg<DK, DV, R>::NT, 0);
+    return e == hipSuccess ? n : 0;
 }
 
 template <int DK, int DV>
