@@ -10,10 +10,20 @@ resident in HBM when timing starts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk C]
                        [--skip-cpu] [--only prefill|decode] [--sweep]
+       python bench.py --calibrate-copy
+       python bench.py --summarize-pmc FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+
+HBM traffic: the figures recorded in profiles/gret_prefill_decode_hbm_traffic.json (rocprofv3
+FETCH_SIZE / WRITE_SIZE per dispatch, scaled by what the same counters read for
+a plain copy of known size) are reported only while the kernel sources hash to
+the values recorded with them; otherwise traffic is null.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +39,99 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix
 METRIC = "gRet prefill tokens/s @N=512K, 24h×128; decode steps/s; % of roofline"
 DEFAULT_CHUNK = 64
+
+
+CSRC = os.path.join(ROOT, "yoco_gated_retention_amd", "csrc")
+# Sources whose change invalidates recorded counter figures, per entry point.
+KERNEL_SOURCES = {
+    "prefill": ["gret_prefill_bf16.hip", "gret_api.cpp", "gret_segments.h", "gret_internal.h",
+                "gret_device.h"],
+    "decode": ["gret_decode.hip", "gret_internal.h", "gret_device.h"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gret_prefill_decode_hbm_traffic.json")
+
+
+def sources_sha256(which):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[which]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(which):
+    """HBM bytes per entry-point call from the committed counter summary, or
+    None when it is missing or was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[which]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_sha256(which):
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def short_kernel_name(name):
+    name = name.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("(")[0]
+
+
+def kernel_group(name):
+    if "decode" in name:
+        return "decode"
+    if "prefill" in name or "combine" in name:
+        return "prefill"
+    return "other:" + name.split("(")[0][:60]
+
+
+def pmc_per_dispatch(d, counter):
+    """Per kernel name: (dispatches, mean counter value per dispatch) from a
+    rocprofv3 --pmc csv output directory."""
+    acc = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = r["Kernel_Name"]
+                n, tot = acc.get(key, (0, 0.0))
+                acc[key] = (n + 1, tot + float(r["Counter_Value"]))
+    return {k: (n, tot / n) for k, (n, tot) in acc.items()}
+
+
+def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    """Scales FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by the plain-copy
+    calibration and sums them per entry-point call (the prefill is three
+    launches: main, combine, prefix)."""
+    copy_bytes = 1 << 30  # --calibrate-copy: 1 GiB read and 1 GiB written per copy
+    cf = [v for k, (n, v) in pmc_per_dispatch(cfetch_dir, "FETCH_SIZE").items() if "copy" in k]
+    cw = [v for k, (n, v) in pmc_per_dispatch(cwrite_dir, "WRITE_SIZE").items() if "copy" in k]
+    if not cf or not cw:
+        raise SystemExit("no copy kernel found in the calibration runs")
+    f_scale = copy_bytes / (max(cf) * 1024.0)
+    w_scale = copy_bytes / (max(cw) * 1024.0)
+    out = {"calibration": {"copy_bytes": copy_bytes, "fetch_kib": max(cf), "write_kib": max(cw),
+                           "fetch_scale": f_scale, "write_scale": w_scale}}
+    fetch = pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = pmc_per_dispatch(write_dir, "WRITE_SIZE")
+    for which in ("prefill", "decode"):
+        names = sorted(k for k in fetch if kernel_group(k) == which)
+        if not names:
+            continue
+        kern = {}
+        for k in names:
+            kern[short_kernel_name(k)] = {
+                "dispatches": fetch[k][0], "fetch_kib": fetch[k][1],
+                "write_kib": write.get(k, (0, float("nan")))[1],
+                "fetch_bytes": fetch[k][1] * 1024.0 * f_scale,
+                "write_bytes": write.get(k, (0, 0.0))[1] * 1024.0 * w_scale}
+        out[which] = {"sources_sha256": sources_sha256(which), "kernels": kern,
+                      "fetch_bytes": sum(x["fetch_bytes"] for x in kern.values()),
+                      "write_bytes": sum(x["write_bytes"] for x in kern.values())}
+    print(json.dumps(out, indent=1))
 
 
 def log(msg):
@@ -135,40 +238,58 @@ def bench_decode(gret, dev, steps_total, reps, warmup_reps):
         "timed_steps": reps * steps_total,
         "roofline": {"kernel": "decode_step_kernel", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": nbytes},
+                     "traffic": recorded_traffic("decode"),
+                     "algorithmic_bytes_per_launch": nbytes},
     }
     del state, q, k, v, lg, out
     torch.cuda.empty_cache()
     return res, d
 
 
-def cpu_prefill_baseline(d, n_sample):
+def cpu_prefill_baseline(d, budget_s):
+    """The oracle's fp64 recurrence over all heads of the prefill workload, on
+    consecutive 64K-position pieces (state carried between them) until about
+    budget_s seconds have passed."""
     import oracle
 
     threads = cpu_threads()
-    sl = {x: np.ascontiguousarray(d[x][:, :, :n_sample]) for x in ("q", "k", "v", "log_gamma")}
-    t0 = time.time()
-    oracle.oracle_prefill_f64(sl["q"], sl["k"], sl["v"], sl["log_gamma"], want_out=False,
-                              nthreads=threads)
-    dt = time.time() - t0
-    B, H = d["q"].shape[:2]
-    return {"value": B * n_sample / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "first %d positions of all %d heads of the 512K workload (fp64 recurrence, "
-                      "%.1f s)" % (n_sample, B * H, dt)}
+    B, H, N = d["q"].shape[:3]
+    piece = 65536
+    state = None
+    done, dt = 0, 0.0
+    while done < N and dt < budget_s:
+        sl = {x: np.ascontiguousarray(d[x][:, :, done:done + piece])
+              for x in ("q", "k", "v", "log_gamma")}
+        t0 = time.time()
+        _, state, _ = oracle.oracle_prefill_f64(sl["q"], sl["k"], sl["v"], sl["log_gamma"],
+                                                state_in=state, want_out=False, nthreads=threads)
+        dt += time.time() - t0
+        done += sl["q"].shape[2]
+    return {"value": B * done / dt, "unit": "tokens/s", "cores": min(threads, B * H),
+            "kind": "oracle",
+            "sample": "positions 0..%d of all %d heads of the %d-position prefill (fp64 "
+                      "recurrence with outputs skipped, %.1f s)" % (done, B * H, N, dt)}
 
 
-def cpu_decode_baseline(d, n_steps):
+def cpu_decode_baseline(d, budget_s):
+    """The oracle's fp64 decode step on all heads, consecutive steps of the
+    decode workload until about budget_s seconds have passed."""
     import oracle
 
     threads = cpu_threads()
     s = d["state"].astype(np.float64)
-    t0 = time.time()
-    for t in range(n_steps):
-        oracle.oracle_decode_f64(d["q"][t], d["k"][t], d["v"][t], d["log_gamma"][t], s,
+    steps = d["q"].shape[0]
+    n, dt = 0, 0.0
+    while n < steps and dt < budget_s:
+        t0 = time.time()
+        oracle.oracle_decode_f64(d["q"][n], d["k"][n], d["v"][n], d["log_gamma"][n], s,
                                  nthreads=threads)
-    dt = time.time() - t0
-    return {"value": n_steps / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": "first %d of the 1000 steps, all 256x24 heads (fp64, %.1f s)" % (n_steps, dt)}
+        dt += time.time() - t0
+        n += 1
+    B, H = d["B"], d["H"]
+    return {"value": n / dt, "unit": "steps/s", "cores": min(threads, B * H), "kind": "oracle",
+            "sample": "first %d of the %d steps, all %dx%d heads (fp64, %.1f s)" % (
+                n, steps, B, H, dt)}
 
 
 def main():
@@ -182,10 +303,18 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=1)
     ap.add_argument("--sweep", action="store_true",
                     help="also time chunk 64/128/256 on the 32K and 512K workloads (stderr)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of each CPU-oracle baseline")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar="DIR", default=None,
+                    help="print HBM traffic per call from rocprofv3 --pmc output directories "
+                         "(FETCH_SIZE run, WRITE_SIZE run, and the two --calibrate-copy runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB (x3) to calibrate the HBM "
                          "traffic counters")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.calibrate_copy:
         import torch
 
@@ -234,7 +363,8 @@ def main():
                        "inputs": "bf16"},
             "roofline": {"kernel": "gret_prefill (main + combine + prefix launches)",
                          "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": recorded_traffic("prefill"),
                          "algorithmic_bytes_per_launch": nbytes,
                          "mfma_tflops": flops / (ms * 1e-3) / 1e12,
                          "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
@@ -253,13 +383,13 @@ def main():
                                     "hbm_frac": nb / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                     "mfma_frac": fl / (m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}))
         if not args.skip_cpu:
-            result["cpu_baseline"] = cpu_prefill_baseline(d3, 131072)
+            result["cpu_baseline"] = cpu_prefill_baseline(d3, args.cpu_seconds)
             log("cpu baseline: %s" % json.dumps(result["cpu_baseline"]))
 
     if args.only in (None, "decode"):
         dec, dd = bench_decode(gret, dev, CONFIGS[5]["decode_steps"], args.decode_reps, 1)
         if not args.skip_cpu:
-            dec["cpu_baseline"] = cpu_decode_baseline(dd, 100)
+            dec["cpu_baseline"] = cpu_decode_baseline(dd, args.cpu_seconds)
         result["decode"] = dec
         log("decode: %.2f us/step, %.0f steps/s, %.0f GB/s (%.1f%%)" % (
             dec["us_per_step"], dec["steps_per_s"], dec["roofline"]["achieved"],
