@@ -60,4 +60,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, const SegPlan& plan);
 // Workgroups per CU the bf16 prefill kernel can keep resident (0 on error).
 int prefill_bf16_blocks_per_cu(int64_t dk, int64_t dv, int64_t chunk);
 
+// The chunk-64 bf16 prefill (gret_prefill_c64.hip), dispatched by the two above.
+hipError_t launch_prefill_bf16_c64(const PrefillArgs& a, const SegPlan& plan);
+int prefill_bf16_c64_blocks_per_cu(int64_t dk, int64_t dv);
+
 }  // namespace gret
