@@ -10,3 +10,4 @@ from .oracle import (  # noqa: F401
     oracle_max_threads,
     oracle_prefill_f64,
 )
+from .output_gate import oracle_output_gate_f64  # noqa: F401
