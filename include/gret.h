@@ -71,7 +71,8 @@ typedef enum {
     GRET_ERR_ALIAS = 4,       /* out overlaps an input, or states overlap
                                  without being identical                      */
     GRET_ERR_HIP = 5,         /* a HIP runtime call or launch failed          */
-    GRET_ERR_WORKSPACE = 6    /* workspace missing, too small or misaligned   */
+    GRET_ERR_WORKSPACE = 6,   /* workspace missing, too small or misaligned   */
+    GRET_ERR_VALUE = 7        /* a scalar argument out of range (norm_eps)    */
 } gret_status_t;
 
 /* Log-gate floor used in place of -inf (gamma ~ 1.8e-35). */
@@ -146,6 +147,42 @@ int gret_prefill(const void* q, const void* k, const void* v, const float* log_g
 int gret_decode_step(const void* q, const void* k, const void* v, const float* log_gamma,
                      const float* state_in, void* out, float* state_out, int64_t B, int64_t H,
                      int64_t dk, int64_t dv, int dtype, void* stream);
+
+/*
+ * Output epilogue of the gated entry points below (page "YOCO 完全拆解：
+ * Decoder-Decoder 架构如何让 KV Cache 只存一次", section "路线二：Multi-Head Gated
+ * Retention", the per-head normalisation and output gate of the multi-head
+ * output). For every (batch, head, position), with o the head's dv retention
+ * outputs at that position:
+ *   mean = sum(o) / dv,  var = sum((o - mean)^2) / dv
+ *   z[j] = (o[j] - mean) / sqrt(var + norm_eps) * w[h][j] + b[h][j]
+ *   y[j] = swish(gate[j]) * z[j],  swish(x) = x / (1 + exp(-x))
+ * i.e. GroupNorm with one group per head over the H*dv channels, an optional
+ * per-channel affine (w = 1 when norm_weight is NULL, b = 0 when norm_bias is
+ * NULL), and the element-wise gate swish(X W_G); y is written to out. The
+ * projection X W_G happens before the call: gate holds its result.
+ *
+ *   gate         same dtype and layout as out ([B,H,N,dv] for prefill, [B,H,dv]
+ *                for decode), required, 16-byte aligned; read only
+ *   norm_weight  fp32 [H,dv] or NULL;  norm_bias  fp32 [H,dv] or NULL
+ *   norm_eps     finite and >= 0, else GRET_ERR_VALUE (torch's GroupNorm
+ *                default is 1e-5); with norm_eps = 0 a constant row divides
+ *                0 by 0
+ * out must not overlap gate, norm_weight or norm_bias (GRET_ERR_ALIAS); every
+ * other argument and rule is that of the plain entry point. The statistics are
+ * computed in fp32 from the fp32 retention output in the decode step, and from
+ * the stored output (dtype) in prefill, which then rewrites out in place.
+ */
+int gret_prefill_gated(const void* q, const void* k, const void* v, const float* log_gamma,
+                       const float* state_in, const void* gate, const float* norm_weight,
+                       const float* norm_bias, float norm_eps, void* out, float* state_out,
+                       int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                       int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+int gret_decode_step_gated(const void* q, const void* k, const void* v, const float* log_gamma,
+                           const float* state_in, const void* gate, const float* norm_weight,
+                           const float* norm_bias, float norm_eps, void* out, float* state_out,
+                           int64_t B, int64_t H, int64_t dk, int64_t dv, int dtype, void* stream);
 
 /* Static, human-readable text for a gret_status_t value (never NULL). */
 const char* gret_status_string(int status);

@@ -12,7 +12,7 @@ import yoco_gated_retention_amd as gret
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gret.h")
 
-OK, NULL, SHAPE, UNSUP, ALIAS, HIP, WORKSPACE = range(7)
+OK, NULL, SHAPE, UNSUP, ALIAS, HIP, WORKSPACE, VALUE = range(8)
 F32, BF16 = 0, 1
 
 
@@ -30,16 +30,16 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"gret_prefill", "gret_decode_step", "gret_prefill_workspace_bytes",
-            "gret_status_string"} <= set(names)
+            "gret_status_string", "gret_prefill_gated", "gret_decode_step_gated"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert gret.gret_status_string(s).startswith(
             ["GRET_OK", "GRET_ERR_NULL", "GRET_ERR_SHAPE", "GRET_ERR_UNSUPPORTED",
-             "GRET_ERR_ALIAS", "GRET_ERR_HIP", "GRET_ERR_WORKSPACE"][s])
+             "GRET_ERR_ALIAS", "GRET_ERR_HIP", "GRET_ERR_WORKSPACE", "GRET_ERR_VALUE"][s])
     assert gret.gret_status_string(99) == "unknown gret status"
 
 
@@ -120,6 +120,40 @@ def test_decode_validation(lib):
     assert decode(lib, out=P(2)) == ALIAS           # out on v
     assert decode(lib, so=ctypes.c_void_p(BASE + 5 * 256 * MB + 1024)) == ALIAS  # partial
     assert decode(lib, so=P(0)) == ALIAS            # state_out on q
+
+
+def prefill_gated(lib, gate=P(8), w=None, b=None, eps=1e-5, out=P(4), dtype=BF16, **kw):
+    a = dict(q=P(0), k=P(1), v=P(2), lg=P(3), si=None, so=P(5), B=1, H=2, N=512, dk=64, dv=64,
+             chunk=64, ws=P(6), wsb=1 << 30)
+    a.update(kw)
+    return lib.gret_prefill_gated(a["q"], a["k"], a["v"], a["lg"], a["si"], gate, w, b,
+                                  ctypes.c_float(eps), out, a["so"], a["B"], a["H"], a["N"],
+                                  a["dk"], a["dv"], a["chunk"], dtype, a["ws"], a["wsb"], None)
+
+
+def decode_gated(lib, gate=P(8), w=None, b=None, eps=1e-5, out=P(4), **kw):
+    a = dict(q=P(0), k=P(1), v=P(2), lg=P(3), si=P(5), so=P(5), B=2, H=3, dk=64, dv=64,
+             dtype=BF16)
+    a.update(kw)
+    return lib.gret_decode_step_gated(a["q"], a["k"], a["v"], a["lg"], a["si"], gate, w, b,
+                                      ctypes.c_float(eps), out, a["so"], a["B"], a["H"],
+                                      a["dk"], a["dv"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("call", [prefill_gated, decode_gated])
+def test_gated_validation(lib, call):
+    assert call(lib, gate=None) == NULL
+    assert call(lib, eps=-1.0) == VALUE
+    assert call(lib, eps=float("nan")) == VALUE
+    assert call(lib, eps=float("inf")) == VALUE
+    assert call(lib, gate=ctypes.c_void_p(BASE + 8 * 256 * MB + 8)) == UNSUP
+    assert call(lib, w=ctypes.c_void_p(BASE + 9 * 256 * MB + 2)) == UNSUP
+    assert call(lib, gate=P(4)) == ALIAS                       # gate on out
+    assert call(lib, w=P(9), out=ctypes.c_void_p(BASE + 9 * 256 * MB + 256)) == ALIAS
+    assert call(lib, b=P(5)) == ALIAS                          # bias on the state
+    assert call(lib, out=None) == NULL
+    # the plain rules still apply
+    assert call(lib, dk=32) == UNSUP
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

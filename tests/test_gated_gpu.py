@@ -1,0 +1,170 @@
+"""GPU parity of the gated entry points (retention + output epilogue) against the
+fp64 oracle chain: oracle recurrence, then the oracle epilogue (per-head
+GroupNorm over dv, optional per-channel affine, swish(gate)).
+
+Bar: eps = max|y - ref| / max|ref| <= 1e-2 for bf16 and <= 1e-4 for fp32, and
+the final state as for the plain entry points. Inputs come from seeded
+generators, never from the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import oracle_output_gate_f64
+from tests.gpu_util import eps, to_dev, to_host
+from workloads import f32_to_bf16_bits, make_decode_inputs, make_prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 1e-2
+TOL_F32 = 1e-4
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def gret():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import yoco_gated_retention_amd as g
+
+    g.load_library()
+    oracle.build_oracle(force=False)
+    return g
+
+
+def seeded_inputs(B, H, N, dk, dv, dtype, seed, s0=True):
+    rng = np.random.default_rng(seed)
+
+    def st(x):
+        return f32_to_bf16_bits(x) if dtype == "bf16" else x.astype(np.float32)
+
+    q = st(rng.standard_normal((B, H, N, dk)).astype(np.float32) / np.sqrt(dk))
+    k = st(rng.standard_normal((B, H, N, dk)).astype(np.float32) / np.sqrt(dk))
+    v = st(rng.standard_normal((B, H, N, dv)).astype(np.float32))
+    u = rng.standard_normal((B, H, N))
+    lg = (-np.logaddexp(0.0, -u) / 16.0).astype(np.float32)
+    S0 = (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32) if s0 else None
+    gate = st((2.0 * rng.standard_normal((B, H, N, dv))).astype(np.float32))
+    w = (1.0 + 0.2 * rng.standard_normal((H, dv))).astype(np.float32)
+    b = (0.2 * rng.standard_normal((H, dv))).astype(np.float32)
+    return dict(q=q, k=k, v=v, log_gamma=lg), S0, gate, w, b
+
+
+def check_prefill_gated(gret, d, S0, gate, w, b, norm_eps, chunk, tol, label=""):
+    B, H, N, dk = d["q"].shape
+    dv = d["v"].shape[3]
+    say("prefill_gated %s B=%d H=%d N=%d dk=%d dv=%d chunk=%d affine=%s eps=%g" % (
+        label, B, H, N, dk, dv, chunk, w is not None, norm_eps))
+    out, st = gret.gret_prefill_gated(
+        to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"]), to_dev(d["log_gamma"]), to_dev(gate),
+        state_in=None if S0 is None else to_dev(S0),
+        norm_weight=None if w is None else to_dev(w), norm_bias=None if b is None else to_dev(b),
+        norm_eps=norm_eps, chunk=chunk)
+    torch.cuda.synchronize()
+    o_ref, s_ref, _ = oracle.oracle_prefill_f64(d["q"], d["k"], d["v"], d["log_gamma"], S0)
+    y_ref = oracle_output_gate_f64(o_ref, gate, w, b, eps=norm_eps)
+    e_y, e_s = eps(to_host(out), y_ref), eps(to_host(st), s_ref)
+    say("   eps_y=%.3e eps_state=%.3e" % (e_y, e_s))
+    assert e_y <= tol and e_s <= tol, (e_y, e_s)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
+@pytest.mark.parametrize("chunk", [64, 256])
+def test_prefill_gated_bf16_dims(gret, dk, dv, chunk):
+    d, S0, gate, w, b = seeded_inputs(2, 3, 1000, dk, dv, "bf16", seed=dk * 7 + dv + chunk)
+    check_prefill_gated(gret, d, S0, gate, w, b, 1e-5, chunk, TOL_BF16, "dims")
+
+
+@pytest.mark.parametrize("affine", [False, True])
+@pytest.mark.parametrize("norm_eps", [1e-5, 0.5])
+def test_prefill_gated_bf16_affine_eps(gret, affine, norm_eps):
+    d, S0, gate, w, b = seeded_inputs(1, 4, 777, 128, 128, "bf16", seed=11, s0=False)
+    check_prefill_gated(gret, d, S0, gate, w if affine else None, b if affine else None,
+                        norm_eps, 64, TOL_BF16, "affine")
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_prefill_gated_f32(gret, chunk):
+    d, S0, gate, w, b = seeded_inputs(1, 2, 600, 64, 64, "f32", seed=21 + chunk)
+    check_prefill_gated(gret, d, S0, gate, w, b, 1e-5, chunk, TOL_F32, "f32")
+
+
+def test_prefill_gated_short_rows(gret):
+    for N in (1, 63, 65):
+        d, S0, gate, w, b = seeded_inputs(1, 3, N, 128, 128, "bf16", seed=N)
+        check_prefill_gated(gret, d, S0, gate, w, b, 1e-5, 64, TOL_BF16, "short")
+
+
+def test_prefill_gated_32k_all_heads(gret):
+    d = make_prefill_inputs(2)
+    rng = np.random.default_rng(2002)
+    H, N, dv = d["q"].shape[1], d["q"].shape[2], d["v"].shape[3]
+    gate = f32_to_bf16_bits((2.0 * rng.standard_normal((1, H, N, dv))).astype(np.float32))
+    w = (1.0 + 0.2 * rng.standard_normal((H, dv))).astype(np.float32)
+    b = (0.2 * rng.standard_normal((H, dv))).astype(np.float32)
+    check_prefill_gated(gret, d, None, gate, w, b, 1e-5, 64, TOL_BF16, "32k")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_decode_gated_small(gret, dtype, dk, dv):
+    rng = np.random.default_rng(dk + 3 * dv + (dtype == "bf16"))
+    B, H, steps = 3, 5, 8
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+
+    def st(x):
+        return f32_to_bf16_bits(x) if dtype == "bf16" else x.astype(np.float32)
+
+    S = (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32)
+    w = (1.0 + 0.2 * rng.standard_normal((H, dv))).astype(np.float32)
+    b = (0.2 * rng.standard_normal((H, dv))).astype(np.float32)
+    state = to_dev(S)
+    s64 = S.astype(np.float64)
+    for t in range(steps):
+        q = st(rng.standard_normal((B, H, dk)).astype(np.float32) / np.sqrt(dk))
+        k = st(rng.standard_normal((B, H, dk)).astype(np.float32) / np.sqrt(dk))
+        v = st(rng.standard_normal((B, H, dv)).astype(np.float32))
+        lg = (-np.logaddexp(0.0, -rng.standard_normal((B, H))) / 16.0).astype(np.float32)
+        gate = st((2.0 * rng.standard_normal((B, H, dv))).astype(np.float32))
+        affine = t % 2 == 0
+        y = gret.gret_decode_step_gated(to_dev(q), to_dev(k), to_dev(v), to_dev(lg), state,
+                                        to_dev(gate), norm_weight=to_dev(w) if affine else None,
+                                        norm_bias=to_dev(b) if affine else None, norm_eps=1e-5)
+        torch.cuda.synchronize()
+        o_ref = oracle.oracle_decode_f64(q, k, v, lg, s64)
+        y_ref = oracle_output_gate_f64(o_ref, gate, w if affine else None,
+                                       b if affine else None, eps=1e-5)
+        e = eps(to_host(y), y_ref)
+        assert e <= tol, (t, e)
+    assert eps(to_host(state), s64) <= tol
+
+
+def test_decode_gated_full_batch_sampled(gret):
+    d = make_decode_inputs(5, steps=20)
+    B, H, dv = d["B"], d["H"], d["dv"]
+    rng = np.random.default_rng(5005)
+    w = (1.0 + 0.2 * rng.standard_normal((H, dv))).astype(np.float32)
+    b = (0.2 * rng.standard_normal((H, dv))).astype(np.float32)
+    state = to_dev(d["state"])
+    sample = (np.arange(B) % 41 == 0)  # every 41st sequence, all heads
+    s64 = d["state"][sample].astype(np.float64)
+    worst = 0.0
+    for t in range(20):
+        gate = f32_to_bf16_bits((2.0 * rng.standard_normal((B, H, dv))).astype(np.float32))
+        y = gret.gret_decode_step_gated(to_dev(d["q"][t]), to_dev(d["k"][t]), to_dev(d["v"][t]),
+                                        to_dev(d["log_gamma"][t]), state, to_dev(gate),
+                                        norm_weight=to_dev(w), norm_bias=to_dev(b))
+        torch.cuda.synchronize()
+        o_ref = oracle.oracle_decode_f64(d["q"][t][sample], d["k"][t][sample],
+                                         d["v"][t][sample], d["log_gamma"][t][sample], s64)
+        y_ref = oracle_output_gate_f64(o_ref, gate[sample], w, b)
+        worst = max(worst, eps(to_host(y)[sample], y_ref))
+    say("decode_gated 256x24 sampled: worst eps_y=%.3e" % worst)
+    assert worst <= TOL_BF16

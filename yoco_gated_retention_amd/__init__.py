@@ -8,9 +8,17 @@ library is not built, every call raises.
 Functions mirror the C ABI names:
   gret_prefill(q, k, v, log_gamma, state_in=None, chunk=64, out=None,
                state_out=None, workspace=None) -> (out, state_out)
+  gret_prefill_gated(q, k, v, log_gamma, gate, state_in=None, norm_weight=None,
+                     norm_bias=None, norm_eps=1e-5, chunk=64, out=None,
+                     state_out=None, workspace=None) -> (out, state_out)
   gret_decode_step(q, k, v, log_gamma, state_in, out=None, state_out=None) -> out
+  gret_decode_step_gated(q, k, v, log_gamma, state_in, gate, norm_weight=None,
+                         norm_bias=None, norm_eps=1e-5, out=None,
+                         state_out=None) -> out
   gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, dtype) -> int
   gret_status_string(status) -> str
+The gated variants add the output epilogue (per-head GroupNorm, optional
+per-channel affine [H, dv] in fp32, element-wise swish(gate)).
 """
 from __future__ import annotations
 
@@ -58,6 +66,13 @@ def load_library():
         lib.gret_prefill_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci,
                                                      ctypes.POINTER(sz)]
         lib.gret_prefill_workspace_bytes.restype = ci
+        fl = ctypes.c_float
+        lib.gret_prefill_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, fl, vp, vp, i64, i64,
+                                           i64, i64, i64, i64, ci, vp, sz, vp]
+        lib.gret_prefill_gated.restype = ci
+        lib.gret_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, fl, vp, vp, i64,
+                                               i64, i64, i64, ci, vp]
+        lib.gret_decode_step_gated.restype = ci
         lib.gret_status_string.argtypes = [ci]
         lib.gret_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -105,11 +120,7 @@ def gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, dtype) -> int:
     return int(n.value)
 
 
-def gret_prefill(q, k, v, log_gamma, state_in=None, chunk=64, out=None, state_out=None,
-                 workspace=None):
-    """Chunkwise prefill. q, k [B,H,N,dk]; v [B,H,N,dv]; log_gamma [B,H,N] fp32;
-    state_in [B,H,dk,dv] fp32 or None. Returns (out [B,H,N,dv], state_out)."""
-    lib = load_library()
+def _prefill_setup(q, k, v, log_gamma, state_in, chunk, out, state_out, workspace):
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(name, t, q.dtype)
     _check_dev("log_gamma", log_gamma, torch.float32)
@@ -136,6 +147,27 @@ def gret_prefill(q, k, v, log_gamma, state_in=None, chunk=64, out=None, state_ou
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (B, H, N, dk, dv, code, out, state_out, workspace, ws_bytes)
+
+
+def _check_epilogue(gate, like, norm_weight, norm_bias, H, dv):
+    _check_dev("gate", gate, like.dtype)
+    if tuple(gate.shape) != tuple(like.shape):
+        raise ValueError("gate must have the output's shape %s" % (tuple(like.shape),))
+    for name, t in (("norm_weight", norm_weight), ("norm_bias", norm_bias)):
+        if t is not None:
+            _check_dev(name, t, torch.float32)
+            if tuple(t.shape) != (H, dv):
+                raise ValueError("%s must be [H, dv]" % name)
+
+
+def gret_prefill(q, k, v, log_gamma, state_in=None, chunk=64, out=None, state_out=None,
+                 workspace=None):
+    """Chunkwise prefill. q, k [B,H,N,dk]; v [B,H,N,dv]; log_gamma [B,H,N] fp32;
+    state_in [B,H,dk,dv] fp32 or None. Returns (out [B,H,N,dv], state_out)."""
+    lib = load_library()
+    B, H, N, dk, dv, code, out, state_out, workspace, ws_bytes = _prefill_setup(
+        q, k, v, log_gamma, state_in, chunk, out, state_out, workspace)
     st = lib.gret_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(state_in), _ptr(out),
                           _ptr(state_out), B, H, N, dk, dv, chunk, code, _ptr(workspace), ws_bytes,
                           _stream())
@@ -144,11 +176,25 @@ def gret_prefill(q, k, v, log_gamma, state_in=None, chunk=64, out=None, state_ou
     return out, state_out
 
 
-def gret_decode_step(q, k, v, log_gamma, state_in, out=None, state_out=None):
-    """One recurrent step. q, k [B,H,dk]; v [B,H,dv]; log_gamma [B,H] fp32;
-    state_in [B,H,dk,dv] fp32 (or None = zero). state_out defaults to state_in
-    (in-place update). Returns out [B,H,dv]."""
+def gret_prefill_gated(q, k, v, log_gamma, gate, state_in=None, norm_weight=None, norm_bias=None,
+                       norm_eps=1e-5, chunk=64, out=None, state_out=None, workspace=None):
+    """Chunkwise prefill followed by the output epilogue: out = swish(gate) *
+    GroupNorm_per_head(retention output). gate [B,H,N,dv] in q's dtype;
+    norm_weight, norm_bias [H,dv] fp32 or None. Returns (out, state_out)."""
     lib = load_library()
+    B, H, N, dk, dv, code, out, state_out, workspace, ws_bytes = _prefill_setup(
+        q, k, v, log_gamma, state_in, chunk, out, state_out, workspace)
+    _check_epilogue(gate, out, norm_weight, norm_bias, H, dv)
+    st = lib.gret_prefill_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(state_in),
+                                _ptr(gate), _ptr(norm_weight), _ptr(norm_bias), float(norm_eps),
+                                _ptr(out), _ptr(state_out), B, H, N, dk, dv, chunk, code,
+                                _ptr(workspace), ws_bytes, _stream())
+    if st != GRET_OK:
+        raise GretError(st, "gret_prefill_gated")
+    return out, state_out
+
+
+def _decode_setup(q, k, v, log_gamma, state_in, out, state_out):
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(name, t, q.dtype)
     _check_dev("log_gamma", log_gamma, torch.float32)
@@ -171,8 +217,33 @@ def gret_decode_step(q, k, v, log_gamma, state_in, out=None, state_out=None):
         out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
     else:
         _check_dev("out", out, q.dtype)
+    return B, H, dk, dv, out, state_out
+
+
+def gret_decode_step(q, k, v, log_gamma, state_in, out=None, state_out=None):
+    """One recurrent step. q, k [B,H,dk]; v [B,H,dv]; log_gamma [B,H] fp32;
+    state_in [B,H,dk,dv] fp32 (or None = zero). state_out defaults to state_in
+    (in-place update). Returns out [B,H,dv]."""
+    lib = load_library()
+    B, H, dk, dv, out, state_out = _decode_setup(q, k, v, log_gamma, state_in, out, state_out)
     st = lib.gret_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(state_in),
                               _ptr(out), _ptr(state_out), B, H, dk, dv, _dtype_code(q), _stream())
     if st != GRET_OK:
         raise GretError(st, "gret_decode_step")
+    return out
+
+
+def gret_decode_step_gated(q, k, v, log_gamma, state_in, gate, norm_weight=None, norm_bias=None,
+                           norm_eps=1e-5, out=None, state_out=None):
+    """One recurrent step with the output epilogue fused into its store:
+    out = swish(gate) * GroupNorm_per_head(q S). gate [B,H,dv] in q's dtype."""
+    lib = load_library()
+    B, H, dk, dv, out, state_out = _decode_setup(q, k, v, log_gamma, state_in, out, state_out)
+    _check_epilogue(gate, out, norm_weight, norm_bias, H, dv)
+    st = lib.gret_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(state_in),
+                                    _ptr(gate), _ptr(norm_weight), _ptr(norm_bias),
+                                    float(norm_eps), _ptr(out), _ptr(state_out), B, H, dk, dv,
+                                    _dtype_code(q), _stream())
+    if st != GRET_OK:
+        raise GretError(st, "gret_decode_step_gated")
     return out

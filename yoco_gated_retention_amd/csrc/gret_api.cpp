@@ -3,6 +3,7 @@
 // HIP runtime, so a rejected call has no side effect at all.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -68,6 +69,28 @@ size_t workspace_need(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, i
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GRET_OK : GRET_ERR_HIP; }
 
+// Checks the output-epilogue arguments; spans of the read-only epilogue
+// tensors go to *sg, *sw, *sb.
+int check_epilogue(const void* gate, const float* w, const float* b, float eps, int64_t rows,
+                   int64_t H, int64_t dv, int64_t esz, Span* sg, Span* sw, Span* sb) {
+    if (!gate) return GRET_ERR_NULL;
+    if (!aligned(gate, 16)) return GRET_ERR_UNSUPPORTED;
+    if ((w && !aligned(w, 4)) || (b && !aligned(b, 4))) return GRET_ERR_UNSUPPORTED;
+    if (!isfinite(eps) || eps < 0.0f) return GRET_ERR_VALUE;
+    *sg = span_of(gate, rows * dv * esz);
+    *sw = span_of(w, H * dv * 4);
+    *sb = span_of(b, H * dv * 4);
+    return GRET_OK;
+}
+
+int prefill_impl(const void* q, const void* k, const void* v, const float* log_gamma,
+                 const float* state_in, const gret::OutputGate* epi, void* out, float* state_out,
+                 int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream);
+int decode_impl(const void* q, const void* k, const void* v, const float* log_gamma,
+                const float* state_in, const gret::OutputGate* epi, void* out, float* state_out,
+                int64_t B, int64_t H, int64_t dk, int64_t dv, int dtype, void* stream);
+
 }  // namespace
 
 namespace gret {
@@ -84,41 +107,12 @@ PrefillWorkspace bf16_workspace_layout(const SegPlan& p, int64_t dk, int64_t dv)
 
 }  // namespace gret
 
-extern "C" {
+namespace {
 
-const char* gret_status_string(int status) {
-    switch (status) {
-        case GRET_OK: return "GRET_OK: success";
-        case GRET_ERR_NULL: return "GRET_ERR_NULL: a required pointer is NULL";
-        case GRET_ERR_SHAPE: return "GRET_ERR_SHAPE: B, H or N is < 1 or the sizes overflow";
-        case GRET_ERR_UNSUPPORTED:
-            return "GRET_ERR_UNSUPPORTED: dk/dv not in {64,128}, chunk not in {64,128,256}, "
-                   "unknown dtype, or a tensor pointer not 16-byte aligned";
-        case GRET_ERR_ALIAS:
-            return "GRET_ERR_ALIAS: out overlaps another buffer, or the states overlap without "
-                   "being identical";
-        case GRET_ERR_HIP: return "GRET_ERR_HIP: a HIP runtime call or kernel launch failed";
-        case GRET_ERR_WORKSPACE:
-            return "GRET_ERR_WORKSPACE: workspace missing, smaller than "
-                   "gret_prefill_workspace_bytes() or not 256-byte aligned";
-        default: return "unknown gret status";
-    }
-}
-
-int gret_prefill_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
-                                 int64_t chunk, int dtype, size_t* bytes) {
-    if (!bytes) return GRET_ERR_NULL;
-    int st = check_common(B, H, N, dk, dv, dtype);
-    if (st != GRET_OK) return st;
-    if (chunk != 64 && chunk != 128 && chunk != 256) return GRET_ERR_UNSUPPORTED;
-    *bytes = workspace_need(B, H, N, dk, dv, chunk, dtype);
-    return GRET_OK;
-}
-
-int gret_prefill(const void* q, const void* k, const void* v, const float* log_gamma,
-                 const float* state_in, void* out, float* state_out, int64_t B, int64_t H,
-                 int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+int prefill_impl(const void* q, const void* k, const void* v, const float* log_gamma,
+                 const float* state_in, const gret::OutputGate* epi, void* out, float* state_out,
+                 int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !log_gamma || !out) return GRET_ERR_NULL;
     int st = check_common(B, H, N, dk, dv, dtype);
     if (st != GRET_OK) return st;
@@ -130,6 +124,12 @@ int gret_prefill(const void* q, const void* k, const void* v, const float* log_g
 
     const int64_t esz = dtype == GRET_DTYPE_BF16 ? 2 : 4;
     const int64_t BHN = B * H * N;
+    Span sg, sgw, sgb;
+    if (epi) {
+        st = check_epilogue(epi->gate, epi->weight, epi->bias, epi->eps, BHN, H, dv, esz, &sg,
+                            &sgw, &sgb);
+        if (st != GRET_OK) return st;
+    }
     const size_t need = workspace_need(B, H, N, dk, dv, chunk, dtype);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
         return GRET_ERR_WORKSPACE;
@@ -147,6 +147,8 @@ int gret_prefill(const void* q, const void* k, const void* v, const float* log_g
     if (overlaps(ss, si) && state_out != state_in) return GRET_ERR_ALIAS;
     for (const Span& x : {sq, sk, sv, sl, si})
         if (overlaps(sw, x)) return GRET_ERR_ALIAS;
+    for (const Span& x : {sg, sgw, sgb})
+        if (overlaps(so, x) || overlaps(ss, x) || overlaps(sw, x)) return GRET_ERR_ALIAS;
 
     gret::PrefillArgs a;
     a.q = q;
@@ -167,7 +169,21 @@ int gret_prefill(const void* q, const void* k, const void* v, const float* log_g
     a.stream = reinterpret_cast<hipStream_t>(stream);
 
     (void)hipGetLastError();  // clear anything pending from unrelated calls
-    if (dtype == GRET_DTYPE_F32) return hip_status(gret::launch_prefill_f32(a));
+    gret::EpilogueArgs ea;
+    if (epi) {
+        ea.out = out;
+        ea.epi = *epi;
+        ea.rows = BHN;
+        ea.H = H;
+        ea.N = N;
+        ea.dv = dv;
+        ea.stream = a.stream;
+    }
+    if (dtype == GRET_DTYPE_F32) {
+        st = hip_status(gret::launch_prefill_f32(a));
+        if (st != GRET_OK || !epi) return st;
+        return hip_status(gret::launch_output_gate_f32(ea));
+    }
 
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return GRET_ERR_HIP;
@@ -178,12 +194,14 @@ int gret_prefill(const void* q, const void* k, const void* v, const float* log_g
     int64_t G = static_cast<int64_t>(cus) * per_cu;
     if (G > gret::kMaxPrefillGroups) G = gret::kMaxPrefillGroups;
     const SegPlan plan = make_plan(B, H, N, chunk, G);
-    return hip_status(gret::launch_prefill_bf16(a, plan));
+    st = hip_status(gret::launch_prefill_bf16(a, plan));
+    if (st != GRET_OK || !epi) return st;
+    return hip_status(gret::launch_output_gate_bf16(ea));
 }
 
-int gret_decode_step(const void* q, const void* k, const void* v, const float* log_gamma,
-                     const float* state_in, void* out, float* state_out, int64_t B, int64_t H,
-                     int64_t dk, int64_t dv, int dtype, void* stream) {
+int decode_impl(const void* q, const void* k, const void* v, const float* log_gamma,
+                const float* state_in, const gret::OutputGate* epi, void* out, float* state_out,
+                int64_t B, int64_t H, int64_t dk, int64_t dv, int dtype, void* stream) {
     if (!q || !k || !v || !log_gamma || !out || !state_out) return GRET_ERR_NULL;
     int st = check_common(B, H, 1, dk, dv, dtype);
     if (st != GRET_OK) return st;
@@ -193,6 +211,12 @@ int gret_decode_step(const void* q, const void* k, const void* v, const float* l
 
     const int64_t esz = dtype == GRET_DTYPE_BF16 ? 2 : 4;
     const int64_t BH = B * H;
+    Span sg, sgw, sgb;
+    if (epi) {
+        st = check_epilogue(epi->gate, epi->weight, epi->bias, epi->eps, BH, H, dv, esz, &sg,
+                            &sgw, &sgb);
+        if (st != GRET_OK) return st;
+    }
     const Span sq = span_of(q, BH * dk * esz), sk = span_of(k, BH * dk * esz),
                sv = span_of(v, BH * dv * esz), sl = span_of(log_gamma, BH * 4),
                so = span_of(out, BH * dv * esz), si = span_of(state_in, BH * dk * dv * 4),
@@ -202,6 +226,8 @@ int gret_decode_step(const void* q, const void* k, const void* v, const float* l
     for (const Span& x : {sq, sk, sv, sl})
         if (overlaps(ss, x)) return GRET_ERR_ALIAS;
     if (overlaps(ss, si) && state_out != state_in) return GRET_ERR_ALIAS;
+    for (const Span& x : {sg, sgw, sgb})
+        if (overlaps(so, x) || overlaps(ss, x)) return GRET_ERR_ALIAS;
 
     gret::DecodeArgs a;
     a.q = q;
@@ -215,10 +241,89 @@ int gret_decode_step(const void* q, const void* k, const void* v, const float* l
     a.H = H;
     a.dk = dk;
     a.dv = dv;
+    if (epi) a.epi = *epi;
     a.stream = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     return hip_status(dtype == GRET_DTYPE_BF16 ? gret::launch_decode_bf16(a)
                                                : gret::launch_decode_f32(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gret_status_string(int status) {
+    switch (status) {
+        case GRET_OK: return "GRET_OK: success";
+        case GRET_ERR_NULL: return "GRET_ERR_NULL: a required pointer is NULL";
+        case GRET_ERR_SHAPE: return "GRET_ERR_SHAPE: B, H or N is < 1 or the sizes overflow";
+        case GRET_ERR_UNSUPPORTED:
+            return "GRET_ERR_UNSUPPORTED: dk/dv not in {64,128}, chunk not in {64,128,256}, "
+                   "unknown dtype, or a tensor pointer not 16-byte aligned";
+        case GRET_ERR_ALIAS:
+            return "GRET_ERR_ALIAS: out overlaps another buffer, or the states overlap without "
+                   "being identical";
+        case GRET_ERR_HIP: return "GRET_ERR_HIP: a HIP runtime call or kernel launch failed";
+        case GRET_ERR_WORKSPACE:
+            return "GRET_ERR_WORKSPACE: workspace missing, smaller than "
+                   "gret_prefill_workspace_bytes() or not 256-byte aligned";
+        case GRET_ERR_VALUE: return "GRET_ERR_VALUE: norm_eps is negative or not finite";
+        default: return "unknown gret status";
+    }
+}
+
+int gret_prefill_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                                 int64_t chunk, int dtype, size_t* bytes) {
+    if (!bytes) return GRET_ERR_NULL;
+    int st = check_common(B, H, N, dk, dv, dtype);
+    if (st != GRET_OK) return st;
+    if (chunk != 64 && chunk != 128 && chunk != 256) return GRET_ERR_UNSUPPORTED;
+    *bytes = workspace_need(B, H, N, dk, dv, chunk, dtype);
+    return GRET_OK;
+}
+
+int gret_prefill(const void* q, const void* k, const void* v, const float* log_gamma,
+                 const float* state_in, void* out, float* state_out, int64_t B, int64_t H,
+                 int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    return prefill_impl(q, k, v, log_gamma, state_in, nullptr, out, state_out, B, H, N, dk, dv,
+                        chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+int gret_prefill_gated(const void* q, const void* k, const void* v, const float* log_gamma,
+                       const float* state_in, const void* gate, const float* norm_weight,
+                       const float* norm_bias, float norm_eps, void* out, float* state_out,
+                       int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                       int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    gret::OutputGate epi;
+    epi.gate = gate;
+    epi.weight = norm_weight;
+    epi.bias = norm_bias;
+    epi.eps = norm_eps;
+    if (!gate) return GRET_ERR_NULL;
+    return prefill_impl(q, k, v, log_gamma, state_in, &epi, out, state_out, B, H, N, dk, dv,
+                        chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+int gret_decode_step(const void* q, const void* k, const void* v, const float* log_gamma,
+                     const float* state_in, void* out, float* state_out, int64_t B, int64_t H,
+                     int64_t dk, int64_t dv, int dtype, void* stream) {
+    return decode_impl(q, k, v, log_gamma, state_in, nullptr, out, state_out, B, H, dk, dv,
+                       dtype, stream);
+}
+
+int gret_decode_step_gated(const void* q, const void* k, const void* v, const float* log_gamma,
+                           const float* state_in, const void* gate, const float* norm_weight,
+                           const float* norm_bias, float norm_eps, void* out, float* state_out,
+                           int64_t B, int64_t H, int64_t dk, int64_t dv, int dtype, void* stream) {
+    gret::OutputGate epi;
+    epi.gate = gate;
+    epi.weight = norm_weight;
+    epi.bias = norm_bias;
+    epi.eps = norm_eps;
+    if (!gate) return GRET_ERR_NULL;
+    return decode_impl(q, k, v, log_gamma, state_in, &epi, out, state_out, B, H, dk, dv, dtype,
+                       stream);
 }
 
 }  // extern "C"

@@ -17,7 +17,11 @@
 //   * the update is fused with the output contraction: each updated float4 is
 //     stored and immediately accumulated into q_i * S[i][:];
 //   * the column sums are reduced across the lanes of a wavefront with
-//     cross-lane shuffles and across the four wavefronts through LDS.
+//     cross-lane shuffles and across the four wavefronts through LDS;
+//   * with an output gate (same page and section: per-head normalisation,
+//     then the element-wise gate swish(X W_G)), the dv outputs of the head,
+//     held in fp32 by the first dv/4 lanes, are normalised (two-pass mean and
+//     variance over those lanes), scaled, gated and then stored.
 #include <hip/hip_runtime.h>
 
 #include "gret_device.h"
@@ -28,11 +32,14 @@ namespace {
 
 constexpr int kDecodeThreads = 256;
 
-template <typename T, int DK, int DV>
+__device__ inline float swish(float x) { return x / (1.0f + __expf(-x)); }
+
+template <typename T, int DK, int DV, bool GATED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ log_gamma, const float* state_in, T* __restrict__ out,
-    float* state_out) {
+    float* state_out, const T* __restrict__ gate, const float* __restrict__ norm_weight,
+    const float* __restrict__ norm_bias, float norm_eps, int64_t H) {
     constexpr int CG = DV / 4;                 // float4 column groups
     constexpr int RG = kDecodeThreads / CG;    // row groups
     constexpr int RPT = DK / RG;               // rows per thread
@@ -113,6 +120,28 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
             o[2] += s_red[w][tid][2];
             o[3] += s_red[w][tid][3];
         }
+        if constexpr (GATED) {
+            // lanes 0..CG-1 of wavefront 0 hold the head's dv outputs
+            float sum = o[0] + o[1] + o[2] + o[3];
+#pragma unroll
+            for (int off = 1; off < CG; off <<= 1) sum += __shfl_xor(sum, off);
+            const float mean = sum * (1.0f / DV);
+            float sq = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sq += (o[i] - mean) * (o[i] - mean);
+#pragma unroll
+            for (int off = 1; off < CG; off <<= 1) sq += __shfl_xor(sq, off);
+            const float rstd = rsqrtf(sq * (1.0f / DV) + norm_eps);
+            const int64_t h = head % H;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = 4 * tid + i;
+                float z = (o[i] - mean) * rstd;
+                if (norm_weight) z *= norm_weight[h * DV + j];
+                if (norm_bias) z += norm_bias[h * DV + j];
+                o[i] = swish(load_as_float(gate, head * DV + j)) * z;
+            }
+        }
         store_from_float(out, head * DV + 4 * tid + 0, o[0]);
         store_from_float(out, head * DV + 4 * tid + 1, o[1]);
         store_from_float(out, head * DV + 4 * tid + 2, o[2]);
@@ -128,11 +157,18 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     const T* k = static_cast<const T*>(a.k);
     const T* v = static_cast<const T*>(a.v);
     T* out = static_cast<T*>(a.out);
-#define GRET_DECODE_CASE(DK_, DV_)                                                            \
-    if (a.dk == DK_ && a.dv == DV_) {                                                         \
-        hipLaunchKernelGGL((decode_step_kernel<T, DK_, DV_>), grid, block, 0, a.stream, q, k, \
-                           v, a.log_gamma, a.state_in, out, a.state_out);                      \
-        return hipGetLastError();                                                             \
+    const T* gate = static_cast<const T*>(a.epi.gate);
+#define GRET_DECODE_CASE(DK_, DV_)                                                             \
+    if (a.dk == DK_ && a.dv == DV_) {                                                          \
+        if (gate)                                                                              \
+            hipLaunchKernelGGL((decode_step_kernel<T, DK_, DV_, true>), grid, block, 0,        \
+                               a.stream, q, k, v, a.log_gamma, a.state_in, out, a.state_out,   \
+                               gate, a.epi.weight, a.epi.bias, a.epi.eps, a.H);                \
+        else                                                                                   \
+            hipLaunchKernelGGL((decode_step_kernel<T, DK_, DV_, false>), grid, block, 0,       \
+                               a.stream, q, k, v, a.log_gamma, a.state_in, out, a.state_out,   \
+                               nullptr, nullptr, nullptr, 0.0f, a.H);                          \
+        return hipGetLastError();                                                              \
     }
     GRET_DECODE_CASE(64, 64)
     GRET_DECODE_CASE(64, 128)

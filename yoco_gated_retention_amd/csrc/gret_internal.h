@@ -30,6 +30,14 @@ struct PrefillArgs {
     hipStream_t stream;
 };
 
+// Output epilogue (per-head GroupNorm + swish gate); gate == nullptr means none.
+struct OutputGate {
+    const void* gate = nullptr;
+    const float* weight = nullptr;  // [H][dv] or null
+    const float* bias = nullptr;    // [H][dv] or null
+    float eps = 0.0f;
+};
+
 struct DecodeArgs {
     const void* q;
     const void* k;
@@ -39,6 +47,16 @@ struct DecodeArgs {
     void* out;
     float* state_out;
     int64_t B, H, dk, dv;
+    OutputGate epi;
+    hipStream_t stream;
+};
+
+// The epilogue applied in place to a stored output: rows = B*H*N rows of dv
+// values each, head of row r = (r / N) % H.
+struct EpilogueArgs {
+    void* out;
+    OutputGate epi;
+    int64_t rows, H, N, dv;
     hipStream_t stream;
 };
 
@@ -59,6 +77,9 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, const SegPlan& plan);
 
 // Workgroups per CU the bf16 prefill kernel can keep resident (0 on error).
 int prefill_bf16_blocks_per_cu(int64_t dk, int64_t dv, int64_t chunk);
+
+hipError_t launch_output_gate_f32(const EpilogueArgs& a);
+hipError_t launch_output_gate_bf16(const EpilogueArgs& a);
 
 // The chunk-64 bf16 prefill (gret_prefill_c64.hip), dispatched by the two above.
 hipError_t launch_prefill_bf16_c64(const PrefillArgs& a, const SegPlan& plan);
