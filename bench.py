@@ -200,6 +200,102 @@ def time_prefill(gret, d, chunk, steps, warmup, dev):
     return ms
 
 
+def time_prefill_gated(gret, d, chunk, steps, warmup, dev, seed=3003):
+    """Plain and gated prefill on the same inputs (gate: seeded normal, bf16;
+    affine: seeded, fp32). The difference of the two call times is the output
+    epilogue's pass."""
+    import torch
+
+    q, k, v = to_dev(d["q"], dev), to_dev(d["k"], dev), to_dev(d["v"], dev)
+    lg = to_dev(d["log_gamma"], dev)
+    B, H, N, dk = d["q"].shape
+    dv = d["v"].shape[3]
+    g = torch.Generator(device=dev).manual_seed(seed)
+    gate = (2.0 * torch.randn((B, H, N, dv), generator=g, device=dev)).to(torch.bfloat16)
+    w = 1.0 + 0.2 * torch.randn((H, dv), generator=g, device=dev)
+    b = 0.2 * torch.randn((H, dv), generator=g, device=dev)
+    out = torch.empty((B, H, N, dv), dtype=torch.bfloat16, device=dev)
+    so = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(gret.gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, 1), 1),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(f):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    plain = timed(lambda: gret.gret_prefill(q, k, v, lg, None, chunk=chunk, out=out, state_out=so,
+                                            workspace=ws))
+    gated = timed(lambda: gret.gret_prefill_gated(q, k, v, lg, gate, norm_weight=w, norm_bias=b,
+                                                  chunk=chunk, out=out, state_out=so,
+                                                  workspace=ws))
+    del q, k, v, lg, gate, out, so, ws
+    torch.cuda.empty_cache()
+    rows = B * H * N
+    epi_bytes = rows * dv * 2 * 3 + 2 * H * dv * 4
+    epi_ms = gated - plain
+    achieved = epi_bytes / (epi_ms * 1e-3) / 1e9 if epi_ms > 0 else None
+    return {"workload": "prefill_gated (same inputs) + per-head GroupNorm + swish gate",
+            "ms_per_call": gated, "plain_ms_per_call": plain, "tokens_per_s": B * N / (gated * 1e-3),
+            "epilogue": {"ms": epi_ms, "algorithmic_bytes": epi_bytes,
+                         "roofline": {"kernel": "output_gate_kernel (in-place pass)", "bound": "hbm",
+                                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": None if achieved is None else achieved / HBM_PEAK_GBS,
+                                      "traffic": None}}}
+
+
+def bench_decode_gated(gret, dev, d, reps=1, seed=4004):
+    """1000 gated decode steps (epilogue fused into the step) on the decode
+    workload, fresh seeded gate values per step."""
+    import torch
+
+    B, H, dk, dv = d["B"], d["H"], d["dk"], d["dv"]
+    steps = d["q"].shape[0]
+    state = to_dev(d["state"], dev)
+    q, k, v, lg = (to_dev(d[x], dev) for x in ("q", "k", "v", "log_gamma"))
+    g = torch.Generator(device=dev).manual_seed(seed)
+    gate = (2.0 * torch.randn((steps, B, H, dv), generator=g, device=dev)).to(torch.bfloat16)
+    w = 1.0 + 0.2 * torch.randn((H, dv), generator=g, device=dev)
+    b = 0.2 * torch.randn((H, dv), generator=g, device=dev)
+    out = torch.empty((B, H, dv), dtype=torch.bfloat16, device=dev)
+
+    def run():
+        for t in range(steps):
+            gret.gret_decode_step_gated(q[t], k[t], v[t], lg[t], state, gate[t], norm_weight=w,
+                                        norm_bias=b, out=out)
+
+    run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / (reps * steps)
+    nbytes = decode_algorithmic(B, H, dk, dv)[0] + B * H * dv * 2 + 2 * H * dv * 4
+    achieved = nbytes / (us * 1e-6) / 1e9
+    del state, q, k, v, lg, gate, out
+    torch.cuda.empty_cache()
+    return {"workload": "decode_gated_b256h24_d128_1000steps", "steps_per_s": 1e6 / us,
+            "us_per_step": us,
+            "roofline": {"kernel": "decode_step_kernel (gated)", "bound": "hbm",
+                         "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "algorithmic_bytes_per_launch": nbytes}}
+
+
 def bench_decode(gret, dev, steps_total, reps, warmup_reps):
     import torch
 
@@ -303,6 +399,8 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=1)
     ap.add_argument("--sweep", action="store_true",
                     help="also time chunk 64/128/256 on the 32K and 512K workloads (stderr)")
+    ap.add_argument("--skip-gated", action="store_true",
+                    help="skip the gated (output epilogue) prefill and decode timings")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of each CPU-oracle baseline")
     ap.add_argument("--summarize-pmc", nargs=4, metavar="DIR", default=None,
@@ -382,6 +480,13 @@ def main():
                                     "tokens_per_s": c["N"] / (m * 1e-3),
                                     "hbm_frac": nb / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                     "mfma_frac": fl / (m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}))
+        if not args.skip_gated:
+            gp = time_prefill_gated(gret, d3, args.chunk, max(5, args.steps // 2), 2, dev)
+            result["prefill_gated"] = gp
+            log("prefill gated: %.3f ms/call (plain %.3f; epilogue pass %.3f ms, %s GB/s)" % (
+                gp["ms_per_call"], gp["plain_ms_per_call"], gp["epilogue"]["ms"],
+                "%.0f" % gp["epilogue"]["roofline"]["achieved"]
+                if gp["epilogue"]["roofline"]["achieved"] else "n/a"))
         if not args.skip_cpu:
             result["cpu_baseline"] = cpu_prefill_baseline(d3, args.cpu_seconds)
             log("cpu baseline: %s" % json.dumps(result["cpu_baseline"]))
@@ -394,6 +499,12 @@ def main():
         log("decode: %.2f us/step, %.0f steps/s, %.0f GB/s (%.1f%%)" % (
             dec["us_per_step"], dec["steps_per_s"], dec["roofline"]["achieved"],
             100 * dec["roofline"]["frac"]))
+        if not args.skip_gated:
+            dg = bench_decode_gated(gret, dev, dd)
+            result["decode_gated"] = dg
+            log("decode gated: %.2f us/step, %.0f steps/s, %.0f GB/s (%.1f%%)" % (
+                dg["us_per_step"], dg["steps_per_s"], dg["roofline"]["achieved"],
+                100 * dg["roofline"]["frac"]))
         if args.only == "decode":
             result.update({"value": dec["steps_per_s"], "unit": "steps/s",
                            "ms_per_step": dec["us_per_step"] / 1000.0,

@@ -9,11 +9,12 @@
 //   z = (o - mean) / sqrt(var + eps) * w[h] + b[h],   y = swish(gate) * z.
 //
 // The kernel is a streaming pass (read the row and its gate, write the row),
-// bound by HBM bandwidth: 3 * dv * sizeof(T) bytes per row. Each lane owns one
-// 16-byte piece of a row, a row is spread over dv * sizeof(T) / 16 adjacent
-// lanes, and its mean and variance (two passes over registers, fp32) are
-// reduced with cross-lane exchanges inside that lane group. Wavefronts stride
-// over the rows.
+// bound by HBM bandwidth: 3 * dv * sizeof(T) bytes per row. A workgroup takes
+// 64 consecutive rows of one head, so the head's affine for a lane's channels
+// is loaded once; each lane owns one 16-byte piece of a row, a row is spread
+// over dv * sizeof(T) / 16 adjacent lanes, and a wavefront issues the loads of
+// all its rows before any arithmetic. Mean and variance (two passes over
+// registers, fp32) are reduced with cross-lane exchanges inside a row's lanes.
 #include <hip/hip_runtime.h>
 
 #include "gret_device.h"
@@ -26,7 +27,8 @@ constexpr int kEpiThreads = 256;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline float swish(float x) { return x / (1.0f + __expf(-x)); }
+// swish(x) = x * sigmoid(x), with the hardware reciprocal (about 1 ulp).
+__device__ inline float swish(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 template <typename T>
 struct Piece;  // one 16-byte piece of a row, widened to fp32
@@ -57,79 +59,96 @@ struct Piece<bf16_t> {
     }
 };
 
+constexpr int kRowsPerGroup = 64;
+
+// Sum over aligned groups of L adjacent lanes (L = 8, 16 or 32), every lane of
+// a group receiving the total. Within a 16-lane DPP row: exchange with lane^1
+// and lane^2 (quad permutations), then with the mirrored lane of the half row
+// and of the row; across rows (L = 32) one cross-lane permute.
+template <int L>
+__device__ inline float group_sum(float v) {
+    static_assert(L == 8 || L == 16 || L == 32, "group size");
+    constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kXor1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kXor2, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kHalfMirror, 0xF, 0xF, false));
+    if constexpr (L >= 16)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kMirror, 0xF, 0xF, false));
+    if constexpr (L == 32) v += __shfl_xor(v, 16);
+    return v;
+}
+
 template <typename T, int DV>
 __global__ __launch_bounds__(kEpiThreads) void output_gate_kernel(
     T* out, const T* __restrict__ gate, const float* __restrict__ weight,
-    const float* __restrict__ bias, float eps, int64_t rows, int64_t H, int64_t N) {
-    constexpr int VPL = Piece<T>::N;  // values per lane
-    constexpr int LPR = DV / VPL;     // lanes per row
-    constexpr int RPW = 64 / LPR;     // rows per wavefront and step
+    const float* __restrict__ bias, float eps, int64_t N, int64_t H, int64_t blocks_per_head) {
+    constexpr int VPL = Piece<T>::N;                // values per lane
+    constexpr int LPR = DV / VPL;                   // lanes per row
+    constexpr int RPW = 64 / LPR;                   // rows per wavefront and step
+    constexpr int WAVES = kEpiThreads / 64;
+    constexpr int STEPS = kRowsPerGroup / (RPW * WAVES);
     static_assert(LPR * VPL == DV && LPR <= 64 && 64 % LPR == 0, "row split");
-    const int lane = threadIdx.x & 63;
-    const int sub = lane / LPR;
+    static_assert(STEPS * RPW * WAVES == kRowsPerGroup, "rows per workgroup");
+    const int64_t bh = blockIdx.x / blocks_per_head;
+    const int64_t n0 = (blockIdx.x - bh * blocks_per_head) * kRowsPerGroup;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c0 = (lane % LPR) * VPL;
-    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kEpiThreads + threadIdx.x) >> 6;
-    const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kEpiThreads) >> 6;
-    for (int64_t r0 = wave * RPW; r0 < rows; r0 += nwaves * RPW) {
-        const int64_t r = r0 + sub;
-        const bool ok = r < rows;  // the same for all lanes of a row
-        float x[VPL], g[VPL];
-        if (ok) {
-            Piece<T>::load(out + r * DV + c0, x);
-            Piece<T>::load(gate + r * DV + c0, g);
+    const int64_t h = bh % H;
+    float w[VPL], b[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        w[i] = weight ? weight[h * DV + c0 + i] : 1.0f;
+        b[i] = bias ? bias[h * DV + c0 + i] : 0.0f;
+    }
+    float x[STEPS][VPL], g[STEPS][VPL];
+    bool ok[STEPS];
+    int64_t off[STEPS];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        const int64_t n = n0 + (s * WAVES + wave) * RPW + lane / LPR;
+        ok[s] = n < N;  // the same for all lanes of a row
+        off[s] = (bh * N + n) * DV + c0;
+        if (ok[s]) {
+            Piece<T>::load(out + off[s], x[s]);
+            Piece<T>::load(gate + off[s], g[s]);
         } else {
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) x[i] = g[i] = 0.0f;
+            for (int i = 0; i < VPL; ++i) x[s][i] = g[s][i] = 0.0f;
         }
-        float s = 0.0f;
+    }
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) s += x[i];
+    for (int s = 0; s < STEPS; ++s) {
+        float sum = 0.0f;
 #pragma unroll
-        for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off);
-        const float mean = s * (1.0f / DV);
-        float q = 0.0f;
+        for (int i = 0; i < VPL; ++i) sum += x[s][i];
+        const float mean = group_sum<LPR>(sum) * (1.0f / DV);
+        float sq = 0.0f;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) q += (x[i] - mean) * (x[i] - mean);
+        for (int i = 0; i < VPL; ++i) sq += (x[s][i] - mean) * (x[s][i] - mean);
+        const float rstd = rsqrtf(group_sum<LPR>(sq) * (1.0f / DV) + eps);
 #pragma unroll
-        for (int off = 1; off < LPR; off <<= 1) q += __shfl_xor(q, off);
-        const float rstd = rsqrtf(q * (1.0f / DV) + eps);
-        if (ok) {
-            const int64_t h = (r / N) % H;
-            const float* wr = weight ? weight + h * DV + c0 : nullptr;
-            const float* br = bias ? bias + h * DV + c0 : nullptr;
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                float z = (x[i] - mean) * rstd;
-                if (wr) z *= wr[i];
-                if (br) z += br[i];
-                x[i] = swish(g[i]) * z;
-            }
-            Piece<T>::store(out + r * DV + c0, x);
-        }
+        for (int i = 0; i < VPL; ++i)
+            x[s][i] = swish(g[s][i]) * ((x[s][i] - mean) * rstd * w[i] + b[i]);
+        if (ok[s]) Piece<T>::store(out + off[s], x[s]);
     }
 }
 
 template <typename T>
 hipError_t launch_t(const EpilogueArgs& a) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return hipErrorInvalidDevice;
-    const int64_t rpw = 64 / (a.dv / Piece<T>::N);
-    const int64_t waves_needed = (a.rows + rpw - 1) / rpw;
-    int64_t blocks = (waves_needed + kEpiThreads / 64 - 1) / (kEpiThreads / 64);
-    const int64_t cap = static_cast<int64_t>(cus > 0 ? cus : 1) * 8;
-    if (blocks > cap) blocks = cap;
+    const int64_t per_head = (a.N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int64_t heads = a.rows / a.N;
+    const int64_t blocks = heads * per_head;
+    if (blocks < 1 || blocks > 0x7fffffff) return hipErrorInvalidValue;
     T* out = static_cast<T*>(a.out);
     const T* gate = static_cast<const T*>(a.epi.gate);
     if (a.dv == 64)
-        hipLaunchKernelGGL((output_gate_kernel<T, 64>), dim3(blocks), dim3(kEpiThreads), 0,
-                           a.stream, out, gate, a.epi.weight, a.epi.bias, a.epi.eps, a.rows, a.H,
-                           a.N);
+        hipLaunchKernelGGL((output_gate_kernel<T, 64>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(kEpiThreads), 0, a.stream, out, gate, a.epi.weight, a.epi.bias,
+                           a.epi.eps, a.N, a.H, per_head);
     else if (a.dv == 128)
-        hipLaunchKernelGGL((output_gate_kernel<T, 128>), dim3(blocks), dim3(kEpiThreads), 0,
-                           a.stream, out, gate, a.epi.weight, a.epi.bias, a.epi.eps, a.rows, a.H,
-                           a.N);
+        hipLaunchKernelGGL((output_gate_kernel<T, 128>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(kEpiThreads), 0, a.stream, out, gate, a.epi.weight, a.epi.bias,
+                           a.epi.eps, a.N, a.H, per_head);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
