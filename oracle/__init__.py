@@ -10,4 +10,5 @@ from .oracle import (  # noqa: F401
     oracle_max_threads,
     oracle_prefill_f64,
 )
+from .cross_attention import oracle_cross_attention_f64  # noqa: F401
 from .output_gate import oracle_output_gate_f64  # noqa: F401
