@@ -47,6 +47,8 @@ KERNEL_SOURCES = {
     "prefill": ["gret_prefill_bf16.hip", "gret_api.cpp", "gret_segments.h", "gret_internal.h",
                 "gret_device.h"],
     "decode": ["gret_decode.hip", "gret_internal.h", "gret_device.h"],
+    "xattn": ["gret_xattn.hip", "gret_internal.h", "gret_device.h"],
+    "epilogue": ["gret_epilogue.hip", "gret_internal.h", "gret_device.h"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gret_prefill_decode_hbm_traffic.json")
 
@@ -80,6 +82,10 @@ def short_kernel_name(name):
 
 
 def kernel_group(name):
+    if "xattn" in name:
+        return "xattn"
+    if "output_gate" in name:
+        return "epilogue"
     if "decode" in name:
         return "decode"
     if "prefill" in name or "combine" in name:
@@ -117,7 +123,7 @@ def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
                            "fetch_scale": f_scale, "write_scale": w_scale}}
     fetch = pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = pmc_per_dispatch(write_dir, "WRITE_SIZE")
-    for which in ("prefill", "decode"):
+    for which in ("prefill", "decode", "xattn", "epilogue"):
         names = sorted(k for k in fetch if kernel_group(k) == which)
         if not names:
             continue
@@ -250,7 +256,7 @@ def time_prefill_gated(gret, d, chunk, steps, warmup, dev, seed=3003):
                          "roofline": {"kernel": "output_gate_kernel (in-place pass)", "bound": "hbm",
                                       "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": None if achieved is None else achieved / HBM_PEAK_GBS,
-                                      "traffic": None}}}
+                                      "traffic": recorded_traffic("epilogue")}}}
 
 
 def bench_decode_gated(gret, dev, d, reps=1, seed=4004):
@@ -294,6 +300,66 @@ def bench_decode_gated(gret, dev, d, reps=1, seed=4004):
                          "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                          "algorithmic_bytes_per_launch": nbytes}}
+
+
+def bench_cross_attention(gret, dev, B, L, reps=20, Hq=24, Hkv=8, d=128, seed=5005,
+                          cpu_seconds=0.0):
+    """Cross-Decoder decode attention over a global KV cache of L positions per
+    sequence (seeded normal q, K, V in bf16; all positions valid)."""
+    import torch
+
+    g = torch.Generator(device=dev).manual_seed(seed)
+    q = torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, L, d), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, L, d), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(gret.gret_cross_attention_workspace_bytes(B, Hq, Hkv, L, d),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        gret.gret_cross_attention_decode(q, k, v, None, None, out=out, workspace=ws)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    nbytes = B * Hkv * L * d * 2 * 2 + 2 * B * Hq * d * 2
+    achieved = nbytes / (us * 1e-6) / 1e9
+    res = {"workload": "cross_attention_decode_b%d_l%d_hq%d_hkv%d_d%d" % (B, L, Hq, Hkv, d),
+           "calls_per_s": 1e6 / us, "us_per_call": us,
+           "roofline": {"kernel": "xattn_split_kernel + xattn_combine_kernel", "bound": "hbm",
+                        "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic("xattn"),
+                        "algorithmic_bytes_per_launch": nbytes}}
+    if cpu_seconds > 0:
+        import oracle
+
+        # the oracle on one sequence's share (host copies of the bf16 bits)
+        qh = q[:1].view(torch.int16).cpu().numpy().view(np.uint16)
+        n_cpu = min(L, 65536)
+        kh = k[:1, :, :n_cpu].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        vh = v[:1, :, :n_cpu].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.time()
+        reps_cpu = 0
+        while time.time() - t0 < cpu_seconds:
+            oracle.oracle_cross_attention_f64(qh, kh, vh)
+            reps_cpu += 1
+        dt = time.time() - t0
+        res["cpu_baseline"] = {"value": reps_cpu * n_cpu / dt, "unit": "cached positions/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": "one sequence, all 24 query heads, first %d positions, "
+                                         "%d calls in %.1f s" % (n_cpu, reps_cpu, dt)}
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_decode(gret, dev, steps_total, reps, warmup_reps):
@@ -395,7 +461,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=DEFAULT_CHUNK)
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "xattn"], default=None)
     ap.add_argument("--decode-reps", type=int, default=1)
     ap.add_argument("--sweep", action="store_true",
                     help="also time chunk 64/128/256 on the 32K and 512K workloads (stderr)")
@@ -491,6 +557,20 @@ def main():
             result["cpu_baseline"] = cpu_prefill_baseline(d3, args.cpu_seconds)
             log("cpu baseline: %s" % json.dumps(result["cpu_baseline"]))
 
+    if args.only in (None, "xattn"):
+        xa = [bench_cross_attention(gret, dev, 1, 524288,
+                                    cpu_seconds=0.0 if args.skip_cpu else 3.0),
+              bench_cross_attention(gret, dev, 16, 32768)]
+        result["cross_attention"] = xa
+        for x in xa:
+            log("cross attention %s: %.1f us/call, %.0f GB/s (%.1f%%)" % (
+                x["workload"], x["us_per_call"], x["roofline"]["achieved"],
+                100 * x["roofline"]["frac"]))
+        if args.only == "xattn":
+            result.update({"value": xa[0]["calls_per_s"], "unit": "calls/s",
+                           "ms_per_step": xa[0]["us_per_call"] / 1000.0,
+                           "config": {"workload": xa[0]["workload"]},
+                           "roofline": xa[0]["roofline"]})
     if args.only in (None, "decode"):
         dec, dd = bench_decode(gret, dev, CONFIGS[5]["decode_steps"], args.decode_reps, 1)
         if not args.skip_cpu:

@@ -72,7 +72,7 @@ typedef enum {
                                  without being identical                      */
     GRET_ERR_HIP = 5,         /* a HIP runtime call or launch failed          */
     GRET_ERR_WORKSPACE = 6,   /* workspace missing, too small or misaligned   */
-    GRET_ERR_VALUE = 7        /* a scalar argument out of range (norm_eps)    */
+    GRET_ERR_VALUE = 7        /* a scalar argument out of range (eps, scale)  */
 } gret_status_t;
 
 /* Log-gate floor used in place of -inf (gamma ~ 1.8e-35). */
@@ -183,6 +183,39 @@ int gret_decode_step_gated(const void* q, const void* k, const void* v, const fl
                            const float* state_in, const void* gate, const float* norm_weight,
                            const float* norm_bias, float norm_eps, void* out, float* state_out,
                            int64_t B, int64_t H, int64_t dk, int64_t dv, int dtype, void* stream);
+
+/*
+ * Cross-Decoder decode attention over the shared global KV cache (page "YOCO
+ * 完全拆解：Decoder-Decoder 架构如何让 KV Cache 只存一次", sections "增量生成时究竟
+ * 追加什么" and "接入推理引擎时的四个关键点": at a decode step each Cross-Decoder
+ * layer's query for the new token attends over the one global cache of keys
+ * and values; with GQA, groups of G = Hq / Hkv query heads share one KV head).
+ * For every sequence b and query head h, with g = h / G:
+ *   out[b,h,:] = softmax_t(scale * q[b,h,:] . k_cache[b,g,t,:]) v_cache[b,g,t,:]
+ * over t < lengths[b] (or t < L when lengths is NULL). Rotary position terms
+ * are applied to q and the cached keys before the call.
+ *
+ *   q          [B,Hq,d] bf16;  out [B,Hq,d] bf16
+ *   k_cache, v_cache  [B,Hkv,L,d] bf16 (L = allocated positions per sequence)
+ *   lengths    device int32 [B] with 1 <= lengths[b] <= L, or NULL (all L);
+ *              values outside that range give unspecified results (memory
+ *              accesses stay inside the caches)
+ *   scale      finite (usually d^-1/2), else GRET_ERR_VALUE
+ *   dtype      GRET_DTYPE_BF16 only (else GRET_ERR_UNSUPPORTED)
+ *   d          64 or 128;  Hq a multiple of Hkv with Hq / Hkv <= 16;  L <= 2^23
+ *   workspace  at least gret_cross_attention_workspace_bytes(...) bytes,
+ *              256-byte aligned (per-range partial results); calls that share
+ *              a workspace must be ordered on one stream
+ * Pointers are 16-byte aligned device pointers (lengths 4-byte); out must not
+ * overlap any other buffer, nor the workspace any input (GRET_ERR_ALIAS).
+ */
+int gret_cross_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
+                                         int64_t d, size_t* bytes);
+
+int gret_cross_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* lengths, void* out, int64_t B, int64_t Hq,
+                                int64_t Hkv, int64_t L, int64_t d, float scale, int dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable text for a gret_status_t value (never NULL). */
 const char* gret_status_string(int status);

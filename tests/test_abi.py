@@ -156,6 +156,33 @@ def test_gated_validation(lib, call):
     assert call(lib, dk=32) == UNSUP
 
 
+def xattn(lib, q=P(0), k=P(1), v=P(2), lens=None, out=P(4), B=2, Hq=24, Hkv=8, L=4096, d=128,
+          scale=0.088, dtype=BF16, ws=P(6), wsb=1 << 30):
+    return lib.gret_cross_attention_decode(q, k, v, lens, out, B, Hq, Hkv, L, d,
+                                           ctypes.c_float(scale), dtype, ws, wsb, None)
+
+
+def test_cross_attention_validation(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.gret_cross_attention_workspace_bytes(2, 24, 8, 4096, 128, ctypes.byref(n)) == OK
+    assert 0 < n.value < 64 << 20 and n.value % 256 == 0
+    assert lib.gret_cross_attention_workspace_bytes(2, 24, 8, 4096, 128, None) == NULL
+    assert xattn(lib, q=None) == NULL
+    assert xattn(lib, L=0) == SHAPE
+    assert xattn(lib, L=(1 << 23) + 1) == SHAPE
+    assert xattn(lib, d=96) == UNSUP
+    assert xattn(lib, Hq=25) == UNSUP                 # not a multiple of Hkv
+    assert xattn(lib, Hq=136) == UNSUP                # 17 query heads per KV head
+    assert xattn(lib, dtype=F32) == UNSUP
+    assert xattn(lib, scale=float("nan")) == VALUE
+    assert xattn(lib, k=ctypes.c_void_p(BASE + 1 * 256 * MB + 8)) == UNSUP
+    assert xattn(lib, lens=ctypes.c_void_p(BASE + 7 * 256 * MB + 2)) == UNSUP
+    assert xattn(lib, ws=None) == WORKSPACE
+    assert xattn(lib, wsb=64) == WORKSPACE
+    assert xattn(lib, out=P(1)) == ALIAS              # out on the key cache
+    assert xattn(lib, ws=P(2)) == ALIAS               # workspace on the value cache
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(gret, "_lib", None)
     monkeypatch.setattr(gret, "LIB_PATH", "/nonexistent/libgret.so")

@@ -16,6 +16,9 @@ Functions mirror the C ABI names:
                          norm_bias=None, norm_eps=1e-5, out=None,
                          state_out=None) -> out
   gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, dtype) -> int
+  gret_cross_attention_decode(q, k_cache, v_cache, lengths=None, scale=None,
+                              out=None, workspace=None) -> out
+  gret_cross_attention_workspace_bytes(B, Hq, Hkv, L, d) -> int
   gret_status_string(status) -> str
 The gated variants add the output epilogue (per-head GroupNorm, optional
 per-channel affine [H, dv] in fp32, element-wise swish(gate)).
@@ -73,6 +76,12 @@ def load_library():
         lib.gret_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, fl, vp, vp, i64,
                                                i64, i64, i64, ci, vp]
         lib.gret_decode_step_gated.restype = ci
+        lib.gret_cross_attention_workspace_bytes.argtypes = [i64, i64, i64, i64, i64,
+                                                             ctypes.POINTER(sz)]
+        lib.gret_cross_attention_workspace_bytes.restype = ci
+        lib.gret_cross_attention_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                                    fl, ci, vp, sz, vp]
+        lib.gret_cross_attention_decode.restype = ci
         lib.gret_status_string.argtypes = [ci]
         lib.gret_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -246,4 +255,50 @@ def gret_decode_step_gated(q, k, v, log_gamma, state_in, gate, norm_weight=None,
                                     _dtype_code(q), _stream())
     if st != GRET_OK:
         raise GretError(st, "gret_decode_step_gated")
+    return out
+
+
+def gret_cross_attention_workspace_bytes(B, Hq, Hkv, L, d) -> int:
+    n = ctypes.c_size_t(0)
+    st = load_library().gret_cross_attention_workspace_bytes(B, Hq, Hkv, L, d, ctypes.byref(n))
+    if st != GRET_OK:
+        raise GretError(st, "gret_cross_attention_workspace_bytes")
+    return int(n.value)
+
+
+def gret_cross_attention_decode(q, k_cache, v_cache, lengths=None, scale=None, out=None,
+                                workspace=None):
+    """Decode attention of q [B,Hq,d] over the global KV cache k_cache, v_cache
+    [B,Hkv,L,d] (bf16), GQA with Hq / Hkv query heads per KV head; lengths: int32
+    [B] on the GPU or None (all L); scale defaults to d^-1/2. Returns out
+    [B,Hq,d] bf16."""
+    lib = load_library()
+    _check_dev("q", q, torch.bfloat16)
+    _check_dev("k_cache", k_cache, torch.bfloat16)
+    _check_dev("v_cache", v_cache, torch.bfloat16)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B,Hq,d] and the caches [B,Hkv,L,d]")
+    B, Hq, d = q.shape
+    _, Hkv, L, dk = k_cache.shape
+    if k_cache.shape[0] != B or dk != d:
+        raise ValueError("cache shape does not match q")
+    if lengths is not None:
+        _check_dev("lengths", lengths, torch.int32)
+        if tuple(lengths.shape) != (B,):
+            raise ValueError("lengths must be [B]")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
+    else:
+        _check_dev("out", out, torch.bfloat16)
+    need = gret_cross_attention_workspace_bytes(B, Hq, Hkv, L, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.gret_cross_attention_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lengths),
+                                         _ptr(out), B, Hq, Hkv, L, d, float(scale),
+                                         GRET_DTYPE_BF16, _ptr(workspace), ws_bytes, _stream())
+    if st != GRET_OK:
+        raise GretError(st, "gret_cross_attention_decode")
     return out

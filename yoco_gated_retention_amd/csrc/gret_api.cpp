@@ -267,7 +267,8 @@ const char* gret_status_string(int status) {
         case GRET_ERR_WORKSPACE:
             return "GRET_ERR_WORKSPACE: workspace missing, smaller than "
                    "gret_prefill_workspace_bytes() or not 256-byte aligned";
-        case GRET_ERR_VALUE: return "GRET_ERR_VALUE: norm_eps is negative or not finite";
+        case GRET_ERR_VALUE:
+            return "GRET_ERR_VALUE: norm_eps is negative or not finite, or scale is not finite";
         default: return "unknown gret status";
     }
 }
@@ -324,6 +325,74 @@ int gret_decode_step_gated(const void* q, const void* k, const void* v, const fl
     if (!gate) return GRET_ERR_NULL;
     return decode_impl(q, k, v, log_gamma, state_in, &epi, out, state_out, B, H, dk, dv, dtype,
                        stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_xattn(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || L < 1) return GRET_ERR_SHAPE;
+    if (B > kMaxElems || Hq > kMaxElems / B || L > (int64_t(1) << 23)) return GRET_ERR_SHAPE;
+    if (B * Hkv > kMaxElems / L / 128 || B * Hq > kMaxElems / 128) return GRET_ERR_SHAPE;
+    if (d != 64 && d != 128) return GRET_ERR_UNSUPPORTED;
+    if (Hq % Hkv != 0 || Hq / Hkv > 16) return GRET_ERR_UNSUPPORTED;
+    return GRET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gret_cross_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
+                                         int64_t d, size_t* bytes) {
+    if (!bytes) return GRET_ERR_NULL;
+    const int st = check_xattn(B, Hq, Hkv, L, d);
+    if (st != GRET_OK) return st;
+    *bytes = gret::xattn_plan(B, Hq, Hkv, L, d).bytes;
+    return GRET_OK;
+}
+
+int gret_cross_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* lengths, void* out, int64_t B, int64_t Hq,
+                                int64_t Hkv, int64_t L, int64_t d, float scale, int dtype,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !out) return GRET_ERR_NULL;
+    int st = check_xattn(B, Hq, Hkv, L, d);
+    if (st != GRET_OK) return st;
+    if (dtype != GRET_DTYPE_BF16) return GRET_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return GRET_ERR_VALUE;
+    for (const void* p : {q, k_cache, v_cache, (const void*)out})
+        if (!aligned(p, 16)) return GRET_ERR_UNSUPPORTED;
+    if (lengths && !aligned(lengths, 4)) return GRET_ERR_UNSUPPORTED;
+    const gret::XAttnPlan plan = gret::xattn_plan(B, Hq, Hkv, L, d);
+    if (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 256))
+        return GRET_ERR_WORKSPACE;
+    const Span sq = span_of(q, B * Hq * d * 2), sk = span_of(k_cache, B * Hkv * L * d * 2),
+               sv = span_of(v_cache, B * Hkv * L * d * 2), sl = span_of(lengths, B * 4),
+               so = span_of(out, B * Hq * d * 2),
+               sw = span_of(workspace, static_cast<int64_t>(plan.bytes));
+    for (const Span& x : {sq, sk, sv, sl, sw})
+        if (overlaps(so, x)) return GRET_ERR_ALIAS;
+    for (const Span& x : {sq, sk, sv, sl})
+        if (overlaps(sw, x)) return GRET_ERR_ALIAS;
+
+    gret::XAttnArgs a;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.lengths = lengths;
+    a.out = out;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.L = L;
+    a.d = d;
+    a.scale = scale;
+    a.workspace = workspace;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return hip_status(gret::launch_xattn_decode(a));
 }
 
 }  // extern "C"

@@ -78,6 +78,28 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, const SegPlan& plan);
 // Workgroups per CU the bf16 prefill kernel can keep resident (0 on error).
 int prefill_bf16_blocks_per_cu(int64_t dk, int64_t dv, int64_t chunk);
 
+// Cross-Decoder decode attention over the global KV cache (gret_xattn.hip).
+struct XAttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* lengths;  // [B] or null (all L)
+    void* out;
+    int64_t B, Hq, Hkv, L, d;
+    float scale;
+    void* workspace;
+    hipStream_t stream;
+};
+// Position ranges per (sequence, KV head) and the workspace they need; the plan
+// depends only on the shapes (not on the device).
+constexpr int64_t kXAttnTargetGroups = 1024;
+struct XAttnPlan {
+    int64_t S = 1, SL = 0;
+    size_t acc_off = 0, bytes = 0;
+};
+XAttnPlan xattn_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d);
+hipError_t launch_xattn_decode(const XAttnArgs& a);
+
 hipError_t launch_output_gate_f32(const EpilogueArgs& a);
 hipError_t launch_output_gate_bf16(const EpilogueArgs& a);
 
