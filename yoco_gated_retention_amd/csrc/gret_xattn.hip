@@ -299,26 +299,65 @@ __global__ __launch_bounds__(kXThreads) void xattn_split_kernel(XParams p) {
 }
 
 // Merges the ranges of every (sequence, query head): out = sum_s e^(m_s - M) a_s
-// / sum_s e^(m_s - M) l_s. One thread per output value.
+// / sum_s e^(m_s - M) l_s. The range weights are computed once into LDS (block
+// reductions for the max and the sum); then every thread accumulates one output
+// value over a share of the ranges, with coalesced, unrolled loads.
+constexpr int kXCombineThreads = 256;
+constexpr int kXMaxRanges = static_cast<int>(kXAttnTargetGroups);
+
+__device__ inline float block_reduce(float v, float* red, bool is_max) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float o = __shfl_xor(v, off);
+        v = is_max ? fmaxf(v, o) : v + o;
+    }
+    __syncthreads();  // red is free
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    v = red[0];
+#pragma unroll
+    for (int i = 1; i < kXCombineThreads / 64; ++i) v = is_max ? fmaxf(v, red[i]) : v + red[i];
+    return v;
+}
+
 template <int D>
-__global__ __launch_bounds__(D) void xattn_combine_kernel(XParams p) {
+__global__ __launch_bounds__(kXCombineThreads) void xattn_combine_kernel(XParams p) {
+    constexpr int PER = kXCombineThreads / D;  // threads per output value
+    __shared__ float sw[kXMaxRanges];
+    __shared__ float red[kXCombineThreads / 64];
+    __shared__ float part[kXCombineThreads];
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / p.Hq, h = bh % p.Hq;
     const int64_t kvh = h / p.G;
     const int gi = static_cast<int>(h % p.G);
-    const int j = threadIdx.x;
     const int64_t base = (b * p.Hkv + kvh) * p.S;
+    const int S = static_cast<int>(p.S);
     float M = -INFINITY;
-    for (int64_t s = 0; s < p.S; ++s) M = fmaxf(M, p.part_ml[(base + s) * p.G + gi].x);
-    float lsum = 0.0f, a = 0.0f;
-    for (int64_t s = 0; s < p.S; ++s) {
+    for (int s = threadIdx.x; s < S; s += kXCombineThreads)
+        M = fmaxf(M, p.part_ml[(base + s) * p.G + gi].x);
+    M = block_reduce(M, red, true);
+    float lsum = 0.0f;
+    for (int s = threadIdx.x; s < S; s += kXCombineThreads) {
         const float2 ml = p.part_ml[(base + s) * p.G + gi];
-        if (ml.x == -INFINITY) continue;
-        const float f = __expf(ml.x - M);
+        const float f = ml.x == -INFINITY ? 0.0f : __expf(ml.x - M);
+        sw[s] = f;
         lsum += f * ml.y;
-        a += f * p.part_acc[((base + s) * p.G + gi) * D + j];
     }
-    p.out[bh * D + j] = to_bf16(a / lsum);
+    lsum = block_reduce(lsum, red, false);  // its barriers also publish sw
+    const int j = threadIdx.x % D, r = threadIdx.x / D;
+    const float* acc = p.part_acc + (base * p.G + gi) * D + j;
+    const int64_t stride = static_cast<int64_t>(p.G) * D;
+    float a = 0.0f;
+#pragma unroll 8
+    for (int s = r; s < S; s += PER) a += sw[s] * acc[s * stride];
+    part[threadIdx.x] = a;
+    __syncthreads();
+    if (r == 0) {
+#pragma unroll
+        for (int k = 1; k < PER; ++k) a += part[k * D + j];
+        p.out[bh * D + j] = to_bf16(a / lsum);
+    }
 }
 
 template <int D>
@@ -344,8 +383,8 @@ hipError_t launch_d(const XAttnArgs& a) {
                        dim3(kXThreads), 0, a.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((xattn_combine_kernel<D>), dim3(static_cast<unsigned>(a.B * a.Hq)), dim3(D),
-                       0, a.stream, p);
+    hipLaunchKernelGGL((xattn_combine_kernel<D>), dim3(static_cast<unsigned>(a.B * a.Hq)),
+                       dim3(kXCombineThreads), 0, a.stream, p);
     return hipGetLastError();
 }
 
