@@ -44,9 +44,10 @@ DEFAULT_CHUNK = 64
 CSRC = os.path.join(ROOT, "yoco_gated_retention_amd", "csrc")
 # Sources whose change invalidates recorded counter figures, per entry point.
 KERNEL_SOURCES = {
-    "prefill": ["gret_prefill_bf16.hip", "gret_api.cpp", "gret_segments.h", "gret_internal.h",
-                "gret_device.h"],
+    "prefill": ["gret_prefill_c64.hip", "gret_prefill_bf16.hip", "gret_prefill_common.h",
+                "gret_api.cpp", "gret_segments.h", "gret_internal.h", "gret_device.h"],
     "decode": ["gret_decode.hip", "gret_internal.h", "gret_device.h"],
+    "decode_gated": ["gret_decode.hip", "gret_internal.h", "gret_device.h"],
     "xattn": ["gret_xattn.hip", "gret_internal.h", "gret_device.h"],
     "epilogue": ["gret_epilogue.hip", "gret_internal.h", "gret_device.h"],
 }
@@ -87,7 +88,9 @@ def kernel_group(name):
     if "output_gate" in name:
         return "epilogue"
     if "decode" in name:
-        return "decode"
+        # the gated instantiation (template flag true; rocprofv3 may leave bf16
+        # instantiations mangled, where the flag reads Lb1E)
+        return "decode_gated" if ("Lb1E" in name or ", true>" in name) else "decode"
     if "prefill" in name or "combine" in name:
         return "prefill"
     return "other:" + name.split("(")[0][:60]
@@ -123,7 +126,7 @@ def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
                            "fetch_scale": f_scale, "write_scale": w_scale}}
     fetch = pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = pmc_per_dispatch(write_dir, "WRITE_SIZE")
-    for which in ("prefill", "decode", "xattn", "epilogue"):
+    for which in ("prefill", "decode", "decode_gated", "xattn", "epilogue"):
         names = sorted(k for k in fetch if kernel_group(k) == which)
         if not names:
             continue
@@ -298,7 +301,8 @@ def bench_decode_gated(gret, dev, d, reps=1, seed=4004):
             "us_per_step": us,
             "roofline": {"kernel": "decode_step_kernel (gated)", "bound": "hbm",
                          "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": recorded_traffic("decode_gated"),
                          "algorithmic_bytes_per_launch": nbytes}}
 
 
