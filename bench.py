@@ -50,6 +50,7 @@ KERNEL_SOURCES = {
     "decode_gated": ["gret_decode.hip", "gret_internal.h", "gret_device.h"],
     "xattn": ["gret_xattn.hip", "gret_internal.h", "gret_device.h"],
     "epilogue": ["gret_epilogue.hip", "gret_internal.h", "gret_device.h"],
+    "proj": ["gret_proj.hip", "gret_internal.h", "gret_device.h"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gret_prefill_decode_hbm_traffic.json")
 
@@ -83,6 +84,8 @@ def short_kernel_name(name):
 
 
 def kernel_group(name):
+    if "proj_kernel" in name:
+        return "proj"
     if "xattn" in name:
         return "xattn"
     if "output_gate" in name:
@@ -126,7 +129,7 @@ def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
                            "fetch_scale": f_scale, "write_scale": w_scale}}
     fetch = pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = pmc_per_dispatch(write_dir, "WRITE_SIZE")
-    for which in ("prefill", "decode", "decode_gated", "xattn", "epilogue"):
+    for which in ("prefill", "decode", "decode_gated", "xattn", "epilogue", "proj"):
         names = sorted(k for k in fetch if kernel_group(k) == which)
         if not names:
             continue
@@ -366,6 +369,78 @@ def bench_cross_attention(gret, dev, B, L, reps=20, Hq=24, Hkv=8, d=128, seed=50
     return res
 
 
+def bench_projection(gret, dev, B=1, N=524288, D=3072, H=24, dk=128, reps=10, seed=7007,
+                     cpu_seconds=0.0):
+    """Key and log-gate projection of the prefill workload's tokens (hidden size
+    3072, 24 heads of 128, gate): x ~ N(0, 1), weights ~ N(0, 1/D), bf16, drawn
+    on the device by a seeded generator. Also times torch's library GEMM on the
+    same product (token-major output, no scaling, no log-gate, no head-major
+    layout) as context."""
+    import torch
+
+    g = torch.Generator(device=dev).manual_seed(seed)
+    x = torch.randn((B, N, D), generator=g, device=dev).to(torch.bfloat16)
+    wk = (torch.randn((H * dk, D), generator=g, device=dev) * D ** -0.5).to(torch.bfloat16)
+    wg = (torch.randn((H, D), generator=g, device=dev) * D ** -0.5).to(torch.bfloat16)
+    k = torch.empty((B, H, N, dk), dtype=torch.bfloat16, device=dev)
+    lg = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(f):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = timed(lambda: gret.gret_head_projection(x, wk, wg, key_scale=dk ** -0.5,
+                                                 temperature=16.0, k_out=k, log_gamma=lg))
+    wcat = torch.cat([wk, wg], 0)
+    x2 = x.view(B * N, D)
+    lib_ms = timed(lambda: torch.matmul(x2, wcat.t()))
+    flops = 2 * B * N * D * (H * dk + H)
+    nbytes = B * N * D * 2 + (H * dk + H) * D * 2 + B * N * H * (dk * 2 + 4)
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {"workload": "key_gate_projection_b%d_n%d_d%d_h%d_dk%d" % (B, N, D, H, dk),
+           "ms_per_call": ms, "tokens_per_s": B * N / (ms * 1e-3),
+           "library_gemm_ms": lib_ms,
+           "roofline": {"kernel": "proj_kernel", "bound": "mfma", "achieved": tf,
+                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tf / BF16_PEAK_TFLOPS, "traffic": recorded_traffic("proj"),
+                        "algorithmic_flops_per_launch": flops,
+                        "algorithmic_bytes_per_launch": nbytes}}
+    if cpu_seconds > 0:
+        import oracle
+        from threadpoolctl import threadpool_limits
+
+        threads = cpu_threads()
+        n_cpu = 512
+        xh = x[:, :n_cpu].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        wkh = wk.view(torch.int16).cpu().numpy().view(np.uint16)
+        wgh = wg.view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.time()
+        calls = 0
+        with threadpool_limits(threads):
+            while time.time() - t0 < cpu_seconds:
+                oracle.oracle_head_projection_f64(xh, wkh, wgh, key_scale=dk ** -0.5,
+                                                  temperature=16.0)
+                calls += 1
+        dt = time.time() - t0
+        res["cpu_baseline"] = {"value": calls * n_cpu / dt, "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": "first %d tokens, all 24 heads and the gate, %d calls "
+                                         "in %.1f s (fp64)" % (n_cpu, calls, dt)}
+    del x, wk, wg, k, lg, wcat
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode(gret, dev, steps_total, reps, warmup_reps):
     import torch
 
@@ -465,7 +540,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=DEFAULT_CHUNK)
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "xattn"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "xattn", "proj"], default=None)
     ap.add_argument("--decode-reps", type=int, default=1)
     ap.add_argument("--sweep", action="store_true",
                     help="also time chunk 64/128/256 on the 32K and 512K workloads (stderr)")
@@ -575,6 +650,17 @@ def main():
                            "ms_per_step": xa[0]["us_per_call"] / 1000.0,
                            "config": {"workload": xa[0]["workload"]},
                            "roofline": xa[0]["roofline"]})
+    if args.only in (None, "proj"):
+        pj = bench_projection(gret, dev, cpu_seconds=0.0 if args.skip_cpu else 3.0)
+        result["projection"] = pj
+        log("key/gate projection: %.3f ms/call, %.0f TFLOP/s (%.1f%% of bf16 peak); library "
+            "GEMM without the epilogue %.3f ms" % (pj["ms_per_call"], pj["roofline"]["achieved"],
+                                                    100 * pj["roofline"]["frac"],
+                                                    pj["library_gemm_ms"]))
+        if args.only == "proj":
+            result.update({"value": pj["tokens_per_s"], "unit": "tokens/s",
+                           "ms_per_step": pj["ms_per_call"],
+                           "config": {"workload": pj["workload"]}, "roofline": pj["roofline"]})
     if args.only in (None, "decode"):
         dec, dd = bench_decode(gret, dev, CONFIGS[5]["decode_steps"], args.decode_reps, 1)
         if not args.skip_cpu:

@@ -217,6 +217,35 @@ int gret_cross_attention_decode(const void* q, const void* k_cache, const void* 
                                 int64_t Hkv, int64_t L, int64_t d, float scale, int dtype,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Key and log-gate projection with the key scaling and the gate's temperature
+ * applied in the product's epilogue (page "YOCO 完全拆解：Decoder-Decoder 架构
+ * 如何让 KV Cache 只存一次", section "路线二：Multi-Head Gated Retention": each
+ * head projects a position's hidden state to its key and to a gate
+ * sigmoid(X W_gamma)^(1/tau); section "单 token Decode 的实现骨架": the key is
+ * scaled by d_h^-1/2 and the gate's log divided by 16). For token m = b*N + n:
+ *   k_out[b,h,n,c]     = key_scale * sum_d x[m,d] * w_key[h*dk + c, d]
+ *   log_gamma[b,h,n]   = log(sigmoid(sum_d x[m,d] * w_gamma[h,d])) / temperature
+ * which are the key and log-gate layouts gret_prefill and gret_decode_step
+ * take. With w_gamma and log_gamma NULL it is a plain head-major projection
+ * (queries, values or the output gate, with key_scale 1 or any other scale).
+ *
+ *   x            [B*N, D] bf16, token-major (row m = hidden state of token m)
+ *   w_key        [H*dk, D] bf16 (row j = weights of output channel j)
+ *   w_gamma      [H, D] bf16, or NULL together with log_gamma
+ *   key_scale    finite; temperature finite and > 0 (else GRET_ERR_VALUE)
+ *   k_out        [B,H,N,dk] bf16 (fp32 accumulation, round to nearest even)
+ *   log_gamma    [B,H,N] fp32
+ *   dtype        GRET_DTYPE_BF16 only (else GRET_ERR_UNSUPPORTED)
+ *   D a multiple of 128 up to 65536; dk a multiple of 16 up to 256; H <= 256
+ *   when the gate is computed (else GRET_ERR_UNSUPPORTED)
+ * Pointers are 16-byte aligned device pointers; k_out and log_gamma must not
+ * overlap each other or any input (GRET_ERR_ALIAS). No workspace.
+ */
+int gret_head_projection(const void* x, const void* w_key, const void* w_gamma, float key_scale,
+                         float temperature, void* k_out, float* log_gamma, int64_t B, int64_t N,
+                         int64_t D, int64_t H, int64_t dk, int dtype, void* stream);
+
 /* Static, human-readable text for a gret_status_t value (never NULL). */
 const char* gret_status_string(int status);
 

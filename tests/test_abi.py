@@ -183,6 +183,33 @@ def test_cross_attention_validation(lib):
     assert xattn(lib, ws=P(2)) == ALIAS               # workspace on the value cache
 
 
+def proj(lib, x=P(0), wk=P(1), wg=P(2), scale=0.088, tau=16.0, k=P(4), lg=P(5), B=1, N=1000,
+         D=3072, H=24, dk=128, dtype=BF16):
+    return lib.gret_head_projection(x, wk, wg, ctypes.c_float(scale), ctypes.c_float(tau), k, lg,
+                                    B, N, D, H, dk, dtype, None)
+
+
+def test_head_projection_validation(lib):
+    assert proj(lib, x=None) == NULL
+    assert proj(lib, k=None) == NULL
+    assert proj(lib, lg=None) == NULL                  # gate weights without the output
+    assert proj(lib, wg=None) == NULL                  # output without the gate weights
+    assert proj(lib, N=0) == SHAPE
+    assert proj(lib, D=65536 + 128) == SHAPE
+    assert proj(lib, D=3000) == UNSUP                  # not a multiple of 128
+    assert proj(lib, dk=72) == UNSUP
+    assert proj(lib, dk=272) == UNSUP
+    assert proj(lib, H=257, dk=16) == UNSUP            # gate heads beyond one tile
+    assert proj(lib, dtype=F32) == UNSUP
+    assert proj(lib, tau=0.0) == VALUE
+    assert proj(lib, tau=float("inf")) == VALUE
+    assert proj(lib, scale=float("nan")) == VALUE
+    assert proj(lib, x=ctypes.c_void_p(BASE + 8)) == UNSUP
+    assert proj(lib, k=P(0)) == ALIAS                  # keys written over x
+    assert proj(lib, lg=P(1)) == ALIAS                 # log-gates over the key weights
+    assert proj(lib, lg=ctypes.c_void_p(BASE + 4 * 256 * MB + 1000 * 3072 * 2 - 256)) == ALIAS
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(gret, "_lib", None)
     monkeypatch.setattr(gret, "LIB_PATH", "/nonexistent/libgret.so")

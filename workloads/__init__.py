@@ -11,5 +11,6 @@ from .gret_inputs import (  # noqa: F401
     f32_to_bf16_bits,
     make_decode_inputs,
     make_prefill_inputs,
+    make_projection_inputs,
     prefill_head,
 )

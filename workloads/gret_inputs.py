@@ -193,3 +193,16 @@ def make_decode_inputs(cfg_id: int = 5, *, B: int | None = None, H: int | None =
         list(ex.map(one, todo))
     return dict(state=state, log_gamma=lg, q=q, k=k, v=v, B=B, H=H, dk=dk, dv=dv, steps=steps,
                 dtype=dtype)
+
+
+def make_projection_inputs(seed: int, B: int, N: int, D: int, H: int, dk: int,
+                           gate: bool = True):
+    """Hidden states x [B, N, D] ~ N(0, 1) and linear-layer weights ~ N(0, 1/D)
+    (keys [H*dk, D], gate [H, D]), all rounded to bf16 (uint16 bits). With
+    these scales every projected value is ~ N(0, 1), the gate logits included."""
+    rng = np.random.default_rng(seed)
+    s = np.float32(1.0 / np.sqrt(D))
+    x = f32_to_bf16_bits(rng.standard_normal((B, N, D), dtype=np.float32))
+    wk = f32_to_bf16_bits(rng.standard_normal((H * dk, D), dtype=np.float32) * s)
+    wg = f32_to_bf16_bits(rng.standard_normal((H, D), dtype=np.float32) * s) if gate else None
+    return x, wk, wg

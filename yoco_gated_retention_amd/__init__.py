@@ -19,6 +19,8 @@ Functions mirror the C ABI names:
   gret_cross_attention_decode(q, k_cache, v_cache, lengths=None, scale=None,
                               out=None, workspace=None) -> out
   gret_cross_attention_workspace_bytes(B, Hq, Hkv, L, d) -> int
+  gret_head_projection(x, w_key, w_gamma=None, key_scale=1.0, temperature=16.0,
+                       H=None, k_out=None, log_gamma=None) -> (k_out, log_gamma)
   gret_status_string(status) -> str
 The gated variants add the output epilogue (per-head GroupNorm, optional
 per-channel affine [H, dv] in fp32, element-wise swish(gate)).
@@ -82,6 +84,9 @@ def load_library():
         lib.gret_cross_attention_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                                     fl, ci, vp, sz, vp]
         lib.gret_cross_attention_decode.restype = ci
+        lib.gret_head_projection.argtypes = [vp, vp, vp, fl, fl, vp, vp, i64, i64, i64, i64, i64,
+                                             ci, vp]
+        lib.gret_head_projection.restype = ci
         lib.gret_status_string.argtypes = [ci]
         lib.gret_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -302,3 +307,48 @@ def gret_cross_attention_decode(q, k_cache, v_cache, lengths=None, scale=None, o
     if st != GRET_OK:
         raise GretError(st, "gret_cross_attention_decode")
     return out
+
+
+def gret_head_projection(x, w_key, w_gamma=None, key_scale=1.0, temperature=16.0, H=None,
+                         k_out=None, log_gamma=None):
+    """Head-major projection of x [B,N,D] (bf16) by w_key [H*dk, D], times
+    key_scale -> k_out [B,H,N,dk] bf16; with w_gamma [H, D] also the log-gate
+    log(sigmoid(x w_gamma^T)) / temperature -> log_gamma [B,H,N] fp32 (else
+    None). H is taken from w_gamma, or must be given without it."""
+    lib = load_library()
+    _check_dev("x", x, torch.bfloat16)
+    _check_dev("w_key", w_key, torch.bfloat16)
+    if x.dim() != 3 or w_key.dim() != 2 or w_key.shape[1] != x.shape[2]:
+        raise ValueError("x must be [B,N,D] and w_key [H*dk, D]")
+    B, N, D = x.shape
+    if w_gamma is not None:
+        _check_dev("w_gamma", w_gamma, torch.bfloat16)
+        if w_gamma.dim() != 2 or w_gamma.shape[1] != D:
+            raise ValueError("w_gamma must be [H, D]")
+        if H is not None and H != w_gamma.shape[0]:
+            raise ValueError("H does not match w_gamma")
+        H = w_gamma.shape[0]
+    if H is None or H < 1 or w_key.shape[0] % H != 0:
+        raise ValueError("w_key must have H * dk rows")
+    dk = w_key.shape[0] // H
+    if k_out is None:
+        k_out = torch.empty((B, H, N, dk), dtype=torch.bfloat16, device=x.device)
+    else:
+        _check_dev("k_out", k_out, torch.bfloat16)
+        if tuple(k_out.shape) != (B, H, N, dk):
+            raise ValueError("k_out must be [B,H,N,dk]")
+    if w_gamma is not None:
+        if log_gamma is None:
+            log_gamma = torch.empty((B, H, N), dtype=torch.float32, device=x.device)
+        else:
+            _check_dev("log_gamma", log_gamma, torch.float32)
+            if tuple(log_gamma.shape) != (B, H, N):
+                raise ValueError("log_gamma must be [B,H,N]")
+    elif log_gamma is not None:
+        raise ValueError("log_gamma needs w_gamma")
+    st = lib.gret_head_projection(_ptr(x), _ptr(w_key), _ptr(w_gamma), float(key_scale),
+                                  float(temperature), _ptr(k_out), _ptr(log_gamma), B, N, D, H,
+                                  dk, GRET_DTYPE_BF16, _stream())
+    if st != GRET_OK:
+        raise GretError(st, "gret_head_projection")
+    return k_out, log_gamma

@@ -395,4 +395,47 @@ int gret_cross_attention_decode(const void* q, const void* k_cache, const void* 
     return hip_status(gret::launch_xattn_decode(a));
 }
 
+int gret_head_projection(const void* x, const void* w_key, const void* w_gamma, float key_scale,
+                         float temperature, void* k_out, float* log_gamma, int64_t B, int64_t N,
+                         int64_t D, int64_t H, int64_t dk, int dtype, void* stream) {
+    if (!x || !w_key || !k_out) return GRET_ERR_NULL;
+    if ((w_gamma == nullptr) != (log_gamma == nullptr)) return GRET_ERR_NULL;
+    if (B < 1 || N < 1 || D < 1 || H < 1 || dk < 1) return GRET_ERR_SHAPE;
+    if (B > kMaxElems / N || H > kMaxElems / dk) return GRET_ERR_SHAPE;
+    const int64_t M = B * N, J = H * dk;
+    if (D > 65536 || M > kMaxElems / D || M > kMaxElems / J) return GRET_ERR_SHAPE;
+    if (dtype != GRET_DTYPE_BF16) return GRET_ERR_UNSUPPORTED;
+    if (D % 128 != 0 || dk % 16 != 0 || dk > 256) return GRET_ERR_UNSUPPORTED;
+    if (w_gamma && H > 256) return GRET_ERR_UNSUPPORTED;
+    if ((M + 255) / 256 * ((J + 255) / 256 + 1) > 0x7fffffff) return GRET_ERR_SHAPE;
+    if (!isfinite(key_scale) || !isfinite(temperature) || !(temperature > 0.0f))
+        return GRET_ERR_VALUE;
+    for (const void* p : {x, w_key, w_gamma, (const void*)k_out, (const void*)log_gamma})
+        if (p && !aligned(p, 16)) return GRET_ERR_UNSUPPORTED;
+    const Span sx = span_of(x, M * D * 2), swk = span_of(w_key, J * D * 2),
+               swg = span_of(w_gamma, H * D * 2), sk = span_of(k_out, M * J * 2),
+               sl = span_of(log_gamma, M * H * 4);
+    for (const Span& s : {sx, swk, swg, sl})
+        if (overlaps(sk, s)) return GRET_ERR_ALIAS;
+    for (const Span& s : {sx, swk, swg})
+        if (overlaps(sl, s)) return GRET_ERR_ALIAS;
+
+    gret::ProjArgs a;
+    a.x = x;
+    a.w_key = w_key;
+    a.w_gamma = w_gamma;
+    a.k_out = k_out;
+    a.log_gamma = log_gamma;
+    a.B = B;
+    a.N = N;
+    a.D = D;
+    a.H = H;
+    a.dk = dk;
+    a.key_scale = key_scale;
+    a.inv_temperature = static_cast<float>(1.0 / static_cast<double>(temperature));
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return hip_status(gret::launch_head_projection(a));
+}
+
 }  // extern "C"

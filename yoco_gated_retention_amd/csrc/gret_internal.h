@@ -103,6 +103,20 @@ hipError_t launch_xattn_decode(const XAttnArgs& a);
 hipError_t launch_output_gate_f32(const EpilogueArgs& a);
 hipError_t launch_output_gate_bf16(const EpilogueArgs& a);
 
+// Key and log-gate projection (gret_proj.hip): x [B*N, D] bf16, weights as
+// rows; keys head-major [B,H,N,dk] bf16 times key_scale, log-gates [B,H,N].
+struct ProjArgs {
+    const void* x;
+    const void* w_key;
+    const void* w_gamma;  // [H, D] or null (no gate)
+    void* k_out;
+    float* log_gamma;     // null iff w_gamma is null
+    int64_t B, N, D, H, dk;
+    float key_scale, inv_temperature;
+    hipStream_t stream;
+};
+hipError_t launch_head_projection(const ProjArgs& a);
+
 // The chunk-64 bf16 prefill (gret_prefill_c64.hip), dispatched by the two above.
 hipError_t launch_prefill_bf16_c64(const PrefillArgs& a, const SegPlan& plan);
 int prefill_bf16_c64_blocks_per_cu(int64_t dk, int64_t dv);
