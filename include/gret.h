@@ -246,6 +246,56 @@ int gret_head_projection(const void* x, const void* w_key, const void* w_gamma, 
                          float temperature, void* k_out, float* log_gamma, int64_t B, int64_t N,
                          int64_t D, int64_t H, int64_t dk, int dtype, void* stream);
 
+/*
+ * Sliding-window-attention Self-Decoder mixer (page "YOCO 完全拆解：Decoder-
+ * Decoder 架构如何让 KV Cache 只存一次", section "路线一：滑动窗口注意力":
+ * position i attends only to the most recent `window` positions, the causal
+ * window mask admitting j in [i - window + 1, i]; decoding keeps only those
+ * keys and values, overwriting the oldest, in a ring (slot p mod window);
+ * section "Prefill 的实现骨架": the prefill leaves the last `window` keys and
+ * values in that fixed buffer). With g = h / (Hq / Hkv):
+ *   out[b,h,i,:] = softmax_j(scale * q[b,h,i,:] . k[b,g,j,:]) v[b,g,j,:]
+ * over max(0, i - window + 1) <= j <= i. Rotary position terms are applied
+ * to q and k before the call.
+ *
+ * gret_swa_prefill:
+ *   q            [B,Hq,N,d] bf16;  out [B,Hq,N,d] bf16 (fp32 softmax)
+ *   k, v         [B,Hkv,N,d] bf16
+ *   k_ring, v_ring  [B,Hkv,window,d] bf16, or both NULL: when given, slot
+ *                p mod window receives position p for the last min(N, window)
+ *                positions (other slots are left as they are)
+ *   N, window    1 .. 2^23;  d 64 or 128;  Hq a multiple of Hkv
+ *   scale        finite (usually d^-1/2), else GRET_ERR_VALUE
+ *   dtype        GRET_DTYPE_BF16 only (else GRET_ERR_UNSUPPORTED)
+ * out and the rings must not overlap each other or an input (GRET_ERR_ALIAS).
+ *
+ * gret_swa_decode_step: one new token per sequence at position positions[b]
+ * (device int32 [B], >= 0; the ring must hold positions
+ * max(0, p - window + 1) .. p - 1 of that sequence, as left by the prefill and
+ * earlier steps). Writes k_new, v_new [B,Hkv,d] into slot p mod window of the
+ * rings (in place), then
+ *   out[b,h,:] = attention of q[b,h,:] over the min(p + 1, window) valid slots.
+ *   q, out       [B,Hq,d] bf16;  Hq / Hkv <= 16;  window <= 2^23
+ *   workspace    at least gret_swa_decode_workspace_bytes(...) bytes, 256-byte
+ *                aligned (valid-slot counts and per-range partial results);
+ *                calls that share a workspace or rings must be ordered on one
+ *                stream
+ * Negative positions give unspecified results; every access stays inside the
+ * rings. Pointers are 16-byte aligned device pointers (positions 4-byte); out,
+ * the workspace and the rings must not overlap any other buffer.
+ */
+int gret_swa_prefill(const void* q, const void* k, const void* v, void* out, void* k_ring,
+                     void* v_ring, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                     int64_t window, float scale, int dtype, void* stream);
+
+int gret_swa_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t window, int64_t d,
+                                    size_t* bytes);
+
+int gret_swa_decode_step(const void* q, const void* k_new, const void* v_new, void* k_ring,
+                         void* v_ring, const int32_t* positions, void* out, int64_t B, int64_t Hq,
+                         int64_t Hkv, int64_t window, int64_t d, float scale, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a gret_status_t value (never NULL). */
 const char* gret_status_string(int status);
 

@@ -210,6 +210,48 @@ def test_head_projection_validation(lib):
     assert proj(lib, lg=ctypes.c_void_p(BASE + 4 * 256 * MB + 1000 * 3072 * 2 - 256)) == ALIAS
 
 
+def swa_pre(lib, q=P(0), k=P(1), v=P(2), out=P(3), rk=P(4), rv=P(5), B=1, Hq=24, Hkv=8, N=4096,
+            d=128, window=1024, scale=0.088, dtype=BF16):
+    return lib.gret_swa_prefill(q, k, v, out, rk, rv, B, Hq, Hkv, N, d, window,
+                                ctypes.c_float(scale), dtype, None)
+
+
+def swa_dec(lib, q=P(0), kn=P(1), vn=P(2), rk=P(3), rv=P(4), pos=P(5), out=P(6), B=4, Hq=24,
+            Hkv=8, window=1024, d=128, scale=0.088, dtype=BF16, ws=P(7), wsb=1 << 30):
+    return lib.gret_swa_decode_step(q, kn, vn, rk, rv, pos, out, B, Hq, Hkv, window, d,
+                                    ctypes.c_float(scale), dtype, ws, wsb, None)
+
+
+def test_swa_validation(lib):
+    assert swa_pre(lib, q=None) == NULL
+    assert swa_pre(lib, rk=None) == NULL              # one ring without the other
+    assert swa_pre(lib, N=0) == SHAPE
+    assert swa_pre(lib, window=0) == SHAPE
+    assert swa_pre(lib, N=(1 << 23) + 1) == SHAPE
+    assert swa_pre(lib, d=96) == UNSUP
+    assert swa_pre(lib, Hq=25) == UNSUP
+    assert swa_pre(lib, dtype=F32) == UNSUP
+    assert swa_pre(lib, scale=float("inf")) == VALUE
+    assert swa_pre(lib, q=ctypes.c_void_p(BASE + 8)) == UNSUP
+    assert swa_pre(lib, out=P(1)) == ALIAS            # out over the keys
+    assert swa_pre(lib, rk=P(2)) == ALIAS             # key ring over the values
+    assert swa_pre(lib, rv=P(4)) == ALIAS             # the rings on each other
+    n = ctypes.c_size_t(0)
+    assert lib.gret_swa_decode_workspace_bytes(4, 24, 8, 1024, 128, ctypes.byref(n)) == OK
+    assert n.value % 256 == 0 and n.value >= 256
+    assert lib.gret_swa_decode_workspace_bytes(4, 24, 8, 1024, 128, None) == NULL
+    assert swa_dec(lib, pos=None) == NULL
+    assert swa_dec(lib, window=0) == SHAPE
+    assert swa_dec(lib, Hq=8 * 17) == UNSUP           # more than 16 query heads per KV head
+    assert swa_dec(lib, pos=ctypes.c_void_p(BASE + 5 * 256 * MB + 2)) == UNSUP
+    assert swa_dec(lib, ws=None) == WORKSPACE
+    assert swa_dec(lib, wsb=256) == WORKSPACE
+    assert swa_dec(lib, out=P(3)) == ALIAS            # out over the key ring
+    assert swa_dec(lib, ws=P(4)) == ALIAS             # workspace over the value ring
+    assert swa_dec(lib, rk=P(0)) == ALIAS             # key ring over q
+    assert swa_dec(lib, scale=float("nan")) == VALUE
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(gret, "_lib", None)
     monkeypatch.setattr(gret, "LIB_PATH", "/nonexistent/libgret.so")

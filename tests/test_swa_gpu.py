@@ -1,0 +1,147 @@
+"""GPU parity of the sliding-window-attention entry points (prefill, the ring
+it leaves, decode steps over the ring) against the fp64 oracle.
+
+Bar: eps = max|x - ref| / max|ref| <= 1e-2 (bf16 inputs and outputs, fp32
+softmax and accumulation); the ring contents are copies and must match
+bit for bit. Inputs come from seeded generators, never from the GPU. Shapes
+cover ragged query tiles, windows below, equal to and above the 256-query
+tile and the prompt, d = 64 and 128, grouped query heads, sequences decoding
+at different positions (ring partly filled and wrapped), and the full-size
+prompt (524288 positions, 24 heads, window 1024) on sampled rows, each of
+which depends only on its own window.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle_swa_decode_f64, oracle_swa_prefill_f64, oracle_swa_ring_f64
+from tests.gpu_util import eps, to_dev, to_host
+from workloads import bf16_bits_to_f32, make_attention_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def gret():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import yoco_gated_retention_amd as g
+
+    g.load_library()
+    return g
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,W", [
+    (1, 2, 2, 300, 128, 64),
+    (2, 4, 2, 1000, 128, 256),
+    (1, 3, 1, 700, 64, 100),
+    (1, 2, 2, 2000, 128, 1024),
+    (1, 1, 1, 50, 128, 1),
+    (1, 2, 2, 130, 128, 4096),
+    (1, 2, 1, 1, 64, 16),
+    (1, 2, 2, 777, 64, 1024),
+])
+def test_swa_prefill_and_ring(gret, B, Hq, Hkv, N, d, W):
+    say("swa_prefill B=%d Hq=%d Hkv=%d N=%d d=%d window=%d" % (B, Hq, Hkv, N, d, W))
+    q, k, v = make_attention_inputs(N + W + d, B, Hq, Hkv, N, d)
+    rk = torch.zeros((B, Hkv, W, d), dtype=torch.bfloat16, device="cuda")
+    rv = torch.zeros_like(rk)
+    out = gret.gret_swa_prefill(to_dev(q), to_dev(k), to_dev(v), W, k_ring=rk, v_ring=rv)
+    torch.cuda.synchronize()
+    ref = oracle_swa_prefill_f64(q, k, v, W)
+    e = eps(to_host(out), ref)
+    say("   eps_out=%.3e" % e)
+    assert e <= TOL
+    wk, wv = oracle_swa_ring_f64(k, v, W)
+    np.testing.assert_array_equal(bf16_bits_to_f32(to_host(rk)), wk)
+    np.testing.assert_array_equal(bf16_bits_to_f32(to_host(rv)), wv)
+
+
+def test_swa_prefill_without_rings(gret):
+    q, k, v = make_attention_inputs(3, 1, 2, 2, 600, 128)
+    out = gret.gret_swa_prefill(to_dev(q), to_dev(k), to_dev(v), 300)
+    torch.cuda.synchronize()
+    assert eps(to_host(out), oracle_swa_prefill_f64(q, k, v, 300)) <= TOL
+
+
+@pytest.mark.parametrize("d,W,Hq,Hkv", [(128, 64, 4, 2), (64, 32, 2, 2), (128, 1024, 3, 1)])
+def test_swa_decode_steps(gret, d, W, Hq, Hkv):
+    """Prefill each sequence to its own length, then decode 6 steps; sequence
+    prompts below, at and above the window."""
+    lens = [W // 2, W, W + 37]
+    B, steps = len(lens), 6
+    T = max(lens) + steps
+    say("swa_decode d=%d window=%d Hq=%d Hkv=%d prompts=%s" % (d, W, Hq, Hkv, lens))
+    q, k, v = make_attention_inputs(d + W + Hq, B, Hq, Hkv, T, d)
+    rk = torch.zeros((B, Hkv, W, d), dtype=torch.bfloat16, device="cuda")
+    rv = torch.zeros_like(rk)
+    for b, n in enumerate(lens):
+        gret.gret_swa_prefill(to_dev(q[b:b + 1, :, :n]), to_dev(k[b:b + 1, :, :n]),
+                              to_dev(v[b:b + 1, :, :n]), W, k_ring=rk[b:b + 1], v_ring=rv[b:b + 1])
+    ref = oracle_swa_prefill_f64(q, k, v, W)  # row t of sequence b is its step at position t
+    ring_k = np.zeros((B, Hkv, W, d))
+    ring_v = np.zeros((B, Hkv, W, d))
+    for b, n in enumerate(lens):
+        a, c = oracle_swa_ring_f64(k[b:b + 1, :, :n], v[b:b + 1, :, :n], W)
+        ring_k[b], ring_v[b] = a[0], c[0]
+    worst = 0.0
+    for s in range(steps):
+        pos = np.array([n + s for n in lens])
+        qs = np.ascontiguousarray(q[np.arange(B), :, pos])
+        ks = np.ascontiguousarray(k[np.arange(B), :, pos])
+        vs = np.ascontiguousarray(v[np.arange(B), :, pos])
+        out = gret.gret_swa_decode_step(to_dev(qs), to_dev(ks), to_dev(vs), rk, rv,
+                                        torch.from_numpy(pos.astype(np.int32)).cuda())
+        torch.cuda.synchronize()
+        o_ref, ring_k, ring_v = oracle_swa_decode_f64(qs, ks, vs, ring_k, ring_v, pos)
+        np.testing.assert_allclose(o_ref, ref[np.arange(B), :, pos], rtol=1e-9, atol=1e-12)
+        worst = max(worst, eps(to_host(out), o_ref))
+    say("   worst eps_out=%.3e" % worst)
+    assert worst <= TOL
+    np.testing.assert_array_equal(bf16_bits_to_f32(to_host(rk)), ring_k)
+    np.testing.assert_array_equal(bf16_bits_to_f32(to_host(rv)), ring_v)
+
+
+def test_swa_prefill_full_size_sampled(gret):
+    """524288 positions, 24 heads of 128, window 1024, inputs drawn on the
+    device by a seeded generator; sampled rows of two heads against the oracle
+    over each row's window."""
+    B, H, N, d, W = 1, 24, 524288, 128, 1024
+    say("swa_prefill full size B=%d H=%d N=%d d=%d window=%d" % (B, H, N, d, W))
+    g = torch.Generator(device="cuda").manual_seed(8008)
+    q = torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+    out = gret.gret_swa_prefill(q, k, v, W)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 1023, 1024, 1025, N - 1],
+                                     rng.integers(0, N, 120)]))
+    worst = 0.0
+    for h in (0, 17):
+        lo = 0
+        for i in rows:
+            j0 = max(0, int(i) - W + 1)
+            qs = to_host(q[0, h, i:i + 1].contiguous())[None, None]
+            ks = to_host(k[0, h, j0:i + 1].contiguous())[None, None]
+            vs = to_host(v[0, h, j0:i + 1].contiguous())[None, None]
+            # the last query of a window-long prompt is row i of the full prompt
+            qq = np.zeros((1, 1, i + 1 - j0, d), np.uint16)
+            qq[0, 0, -1] = qs[0, 0, 0]
+            r = oracle_swa_prefill_f64(qq, ks, vs, W)[0, 0, -1]
+            got = to_host(out[0, h, i].contiguous())
+            worst = max(worst, eps(got, r))
+            lo += 1
+    say("   sampled %d rows x 2 heads: worst eps_out=%.3e" % (len(rows), worst))
+    assert worst <= TOL
+    del q, k, v, out
+    torch.cuda.empty_cache()

@@ -9,6 +9,7 @@ from .gret_inputs import (  # noqa: F401
     LN_SHARP_GAMMA,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    make_attention_inputs,
     make_decode_inputs,
     make_prefill_inputs,
     make_projection_inputs,

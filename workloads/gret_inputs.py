@@ -206,3 +206,13 @@ def make_projection_inputs(seed: int, B: int, N: int, D: int, H: int, dk: int,
     wk = f32_to_bf16_bits(rng.standard_normal((H * dk, D), dtype=np.float32) * s)
     wg = f32_to_bf16_bits(rng.standard_normal((H, D), dtype=np.float32) * s) if gate else None
     return x, wk, wg
+
+
+def make_attention_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int):
+    """Queries [B, Hq, N, d] and keys, values [B, Hkv, N, d], all ~ N(0, 1) and
+    rounded to bf16 (uint16 bits): the shapes of a sliding-window layer."""
+    rng = np.random.default_rng(seed)
+    q = f32_to_bf16_bits(rng.standard_normal((B, Hq, N, d), dtype=np.float32))
+    k = f32_to_bf16_bits(rng.standard_normal((B, Hkv, N, d), dtype=np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((B, Hkv, N, d), dtype=np.float32))
+    return q, k, v

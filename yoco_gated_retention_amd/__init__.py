@@ -21,6 +21,11 @@ Functions mirror the C ABI names:
   gret_cross_attention_workspace_bytes(B, Hq, Hkv, L, d) -> int
   gret_head_projection(x, w_key, w_gamma=None, key_scale=1.0, temperature=16.0,
                        H=None, k_out=None, log_gamma=None) -> (k_out, log_gamma)
+  gret_swa_prefill(q, k, v, window, scale=None, out=None, k_ring=None,
+                   v_ring=None) -> out
+  gret_swa_decode_step(q, k_new, v_new, k_ring, v_ring, positions, scale=None,
+                       out=None, workspace=None) -> out
+  gret_swa_decode_workspace_bytes(B, Hq, Hkv, window, d) -> int
   gret_status_string(status) -> str
 The gated variants add the output epilogue (per-head GroupNorm, optional
 per-channel affine [H, dv] in fp32, element-wise swish(gate)).
@@ -87,6 +92,15 @@ def load_library():
         lib.gret_head_projection.argtypes = [vp, vp, vp, fl, fl, vp, vp, i64, i64, i64, i64, i64,
                                              ci, vp]
         lib.gret_head_projection.restype = ci
+        lib.gret_swa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, fl,
+                                         ci, vp]
+        lib.gret_swa_prefill.restype = ci
+        lib.gret_swa_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64,
+                                                        ctypes.POINTER(sz)]
+        lib.gret_swa_decode_workspace_bytes.restype = ci
+        lib.gret_swa_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                             fl, ci, vp, sz, vp]
+        lib.gret_swa_decode_step.restype = ci
         lib.gret_status_string.argtypes = [ci]
         lib.gret_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -352,3 +366,81 @@ def gret_head_projection(x, w_key, w_gamma=None, key_scale=1.0, temperature=16.0
     if st != GRET_OK:
         raise GretError(st, "gret_head_projection")
     return k_out, log_gamma
+
+
+def gret_swa_prefill(q, k, v, window, scale=None, out=None, k_ring=None, v_ring=None):
+    """Sliding-window causal attention of q [B,Hq,N,d] over k, v [B,Hkv,N,d]
+    (bf16) with `window` positions per query; fills k_ring, v_ring
+    [B,Hkv,window,d] with the last positions when given. Returns out."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, torch.bfloat16)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,Hq,N,d] and k, v [B,Hkv,N,d]")
+    B, Hq, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError("k, v do not match q")
+    Hkv = k.shape[1]
+    if (k_ring is None) != (v_ring is None):
+        raise ValueError("give both rings or neither")
+    if k_ring is not None:
+        for name, t in (("k_ring", k_ring), ("v_ring", v_ring)):
+            _check_dev(name, t, torch.bfloat16)
+            if tuple(t.shape) != (B, Hkv, window, d):
+                raise ValueError("%s must be [B,Hkv,window,d]" % name)
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_dev("out", out, torch.bfloat16)
+    st = lib.gret_swa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(k_ring), _ptr(v_ring),
+                              B, Hq, Hkv, N, d, int(window), float(scale), GRET_DTYPE_BF16,
+                              _stream())
+    if st != GRET_OK:
+        raise GretError(st, "gret_swa_prefill")
+    return out
+
+
+def gret_swa_decode_workspace_bytes(B, Hq, Hkv, window, d) -> int:
+    n = ctypes.c_size_t(0)
+    st = load_library().gret_swa_decode_workspace_bytes(B, Hq, Hkv, window, d, ctypes.byref(n))
+    if st != GRET_OK:
+        raise GretError(st, "gret_swa_decode_workspace_bytes")
+    return int(n.value)
+
+
+def gret_swa_decode_step(q, k_new, v_new, k_ring, v_ring, positions, scale=None, out=None,
+                         workspace=None):
+    """One decode step of sliding-window attention: k_new, v_new [B,Hkv,d] go
+    into ring slot positions[b] mod window (rings [B,Hkv,window,d], updated in
+    place), then q [B,Hq,d] attends over the valid slots. positions: int32 [B]
+    on the GPU. Returns out [B,Hq,d] bf16."""
+    lib = load_library()
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_ring", k_ring),
+                    ("v_ring", v_ring)):
+        _check_dev(name, t, torch.bfloat16)
+    _check_dev("positions", positions, torch.int32)
+    if q.dim() != 3 or k_ring.dim() != 4 or v_ring.shape != k_ring.shape:
+        raise ValueError("q must be [B,Hq,d] and the rings [B,Hkv,window,d]")
+    B, Hq, d = q.shape
+    _, Hkv, window, dr = k_ring.shape
+    if k_ring.shape[0] != B or dr != d or tuple(k_new.shape) != (B, Hkv, d) or \
+            v_new.shape != k_new.shape or tuple(positions.shape) != (B,):
+        raise ValueError("shapes do not match")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_dev("out", out, torch.bfloat16)
+    need = gret_swa_decode_workspace_bytes(B, Hq, Hkv, window, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.gret_swa_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_ring), _ptr(v_ring),
+                                  _ptr(positions), _ptr(out), B, Hq, Hkv, window, d, float(scale),
+                                  GRET_DTYPE_BF16, _ptr(workspace), ws_bytes, _stream())
+    if st != GRET_OK:
+        raise GretError(st, "gret_swa_decode_step")
+    return out

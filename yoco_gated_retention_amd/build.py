@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgret.so")
 SOURCES = ["gret_api.cpp", "gret_decode.hip", "gret_prefill_f32.hip", "gret_prefill_bf16.hip",
-           "gret_prefill_c64.hip", "gret_epilogue.hip", "gret_xattn.hip", "gret_proj.hip"]
+           "gret_prefill_c64.hip", "gret_epilogue.hip", "gret_xattn.hip", "gret_proj.hip", "gret_swa.hip"]
 ARCH = "gfx950"
 
 

@@ -439,3 +439,138 @@ int gret_head_projection(const void* x, const void* w_key, const void* w_gamma, 
 }
 
 }  // extern "C"
+
+namespace {
+constexpr int64_t kSwaMaxN = int64_t(1) << 23;
+
+int check_swa(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t window, int dtype) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || window < 1) return GRET_ERR_SHAPE;
+    if (B > kMaxElems / Hq || window > kSwaMaxN) return GRET_ERR_SHAPE;
+    if (!head_dim_ok(d) || Hq % Hkv != 0) return GRET_ERR_UNSUPPORTED;
+    if (dtype != GRET_DTYPE_BF16) return GRET_ERR_UNSUPPORTED;
+    return GRET_OK;
+}
+
+size_t swa_lengths_bytes(int64_t B) { return (static_cast<size_t>(B) * 4 + 255) / 256 * 256; }
+}  // namespace
+
+extern "C" {
+
+int gret_swa_prefill(const void* q, const void* k, const void* v, void* out, void* k_ring,
+                     void* v_ring, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                     int64_t window, float scale, int dtype, void* stream) {
+    if (!q || !k || !v || !out) return GRET_ERR_NULL;
+    if ((k_ring == nullptr) != (v_ring == nullptr)) return GRET_ERR_NULL;
+    int st = check_swa(B, Hq, Hkv, d, window, dtype);
+    if (st != GRET_OK) return st;
+    if (N < 1 || N > kSwaMaxN) return GRET_ERR_SHAPE;
+    if (!isfinite(scale)) return GRET_ERR_VALUE;
+    for (const void* p : {q, k, v, (const void*)out, (const void*)k_ring, (const void*)v_ring})
+        if (p && !aligned(p, 16)) return GRET_ERR_UNSUPPORTED;
+    const Span sq = span_of(q, B * Hq * N * d * 2), sk = span_of(k, B * Hkv * N * d * 2),
+               sv = span_of(v, B * Hkv * N * d * 2), so = span_of(out, B * Hq * N * d * 2),
+               srk = span_of(k_ring, B * Hkv * window * d * 2),
+               srv = span_of(v_ring, B * Hkv * window * d * 2);
+    for (const Span& x : {sq, sk, sv, srk, srv})
+        if (overlaps(so, x)) return GRET_ERR_ALIAS;
+    for (const Span& x : {sq, sk, sv, srv})
+        if (overlaps(srk, x)) return GRET_ERR_ALIAS;
+    for (const Span& x : {sq, sk, sv})
+        if (overlaps(srv, x)) return GRET_ERR_ALIAS;
+
+    gret::SwaArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.k_ring = k_ring;
+    a.v_ring = v_ring;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.d = d;
+    a.window = window;
+    a.scale = scale;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return hip_status(gret::launch_swa_prefill(a));
+}
+
+int gret_swa_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t window, int64_t d,
+                                    size_t* bytes) {
+    if (!bytes) return GRET_ERR_NULL;
+    int st = check_swa(B, Hq, Hkv, d, window, GRET_DTYPE_BF16);
+    if (st != GRET_OK) return st;
+    st = check_xattn(B, Hq, Hkv, window, d);
+    if (st != GRET_OK) return st;
+    *bytes = swa_lengths_bytes(B) + gret::xattn_plan(B, Hq, Hkv, window, d).bytes;
+    return GRET_OK;
+}
+
+int gret_swa_decode_step(const void* q, const void* k_new, const void* v_new, void* k_ring,
+                         void* v_ring, const int32_t* positions, void* out, int64_t B, int64_t Hq,
+                         int64_t Hkv, int64_t window, int64_t d, float scale, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k_new || !v_new || !k_ring || !v_ring || !positions || !out) return GRET_ERR_NULL;
+    int st = check_swa(B, Hq, Hkv, d, window, dtype);
+    if (st != GRET_OK) return st;
+    st = check_xattn(B, Hq, Hkv, window, d);
+    if (st != GRET_OK) return st;
+    if (!isfinite(scale)) return GRET_ERR_VALUE;
+    for (const void* p : {q, k_new, v_new, (const void*)k_ring, (const void*)v_ring,
+                          (const void*)out})
+        if (!aligned(p, 16)) return GRET_ERR_UNSUPPORTED;
+    if (!aligned(positions, 4)) return GRET_ERR_UNSUPPORTED;
+    const size_t lbytes = swa_lengths_bytes(B);
+    const gret::XAttnPlan plan = gret::xattn_plan(B, Hq, Hkv, window, d);
+    if (!workspace || workspace_bytes < lbytes + plan.bytes || !aligned(workspace, 256))
+        return GRET_ERR_WORKSPACE;
+    const Span sq = span_of(q, B * Hq * d * 2), skn = span_of(k_new, B * Hkv * d * 2),
+               svn = span_of(v_new, B * Hkv * d * 2),
+               srk = span_of(k_ring, B * Hkv * window * d * 2),
+               srv = span_of(v_ring, B * Hkv * window * d * 2), sp = span_of(positions, B * 4),
+               so = span_of(out, B * Hq * d * 2),
+               sw = span_of(workspace, static_cast<int64_t>(lbytes + plan.bytes));
+    for (const Span& x : {sq, skn, svn, srk, srv, sp, sw})
+        if (overlaps(so, x)) return GRET_ERR_ALIAS;
+    for (const Span& x : {sq, skn, svn, srk, srv, sp})
+        if (overlaps(sw, x)) return GRET_ERR_ALIAS;
+    for (const Span& x : {sq, skn, svn, srv, sp})
+        if (overlaps(srk, x)) return GRET_ERR_ALIAS;
+    for (const Span& x : {sq, skn, svn, sp})
+        if (overlaps(srv, x)) return GRET_ERR_ALIAS;
+
+    gret::SwaDecodeArgs da;
+    da.k_new = k_new;
+    da.v_new = v_new;
+    da.k_ring = k_ring;
+    da.v_ring = v_ring;
+    da.positions = positions;
+    da.B = B;
+    da.Hkv = Hkv;
+    da.d = d;
+    da.window = window;
+    da.stream = reinterpret_cast<hipStream_t>(stream);
+    int32_t* lengths = static_cast<int32_t*>(workspace);
+    (void)hipGetLastError();
+    st = hip_status(gret::launch_swa_append(da, lengths));
+    if (st != GRET_OK) return st;
+    gret::XAttnArgs a;
+    a.q = q;
+    a.k = k_ring;
+    a.v = v_ring;
+    a.lengths = lengths;
+    a.out = out;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.L = window;
+    a.d = d;
+    a.scale = scale;
+    a.workspace = static_cast<char*>(workspace) + lbytes;
+    a.stream = da.stream;
+    return hip_status(gret::launch_xattn_decode(a));
+}
+
+}  // extern "C"

@@ -117,6 +117,31 @@ struct ProjArgs {
 };
 hipError_t launch_head_projection(const ProjArgs& a);
 
+// Sliding-window attention Self-Decoder (gret_swa.hip): prefill over the
+// prompt (and the ring buffers it leaves), decode-step append into the rings.
+struct SwaArgs {
+    const void* q;   // [B,Hq,N,d]
+    const void* k;   // [B,Hkv,N,d]
+    const void* v;
+    void* out;       // [B,Hq,N,d]
+    void* k_ring;    // [B,Hkv,window,d] or null (then v_ring is null too)
+    void* v_ring;
+    int64_t B, Hq, Hkv, N, d, window;
+    float scale;
+    hipStream_t stream;
+};
+hipError_t launch_swa_prefill(const SwaArgs& a);
+struct SwaDecodeArgs {
+    const void* k_new;  // [B,Hkv,d]
+    const void* v_new;
+    void* k_ring;       // [B,Hkv,window,d]
+    void* v_ring;
+    const int32_t* positions;  // [B]
+    int64_t B, Hkv, d, window;
+    hipStream_t stream;
+};
+hipError_t launch_swa_append(const SwaDecodeArgs& a, int32_t* lengths);
+
 // The chunk-64 bf16 prefill (gret_prefill_c64.hip), dispatched by the two above.
 hipError_t launch_prefill_bf16_c64(const PrefillArgs& a, const SegPlan& plan);
 int prefill_bf16_c64_blocks_per_cu(int64_t dk, int64_t dv);
