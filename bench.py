@@ -51,6 +51,7 @@ KERNEL_SOURCES = {
     "xattn": ["gret_xattn.hip", "gret_internal.h", "gret_device.h"],
     "epilogue": ["gret_epilogue.hip", "gret_internal.h", "gret_device.h"],
     "proj": ["gret_proj.hip", "gret_internal.h", "gret_device.h"],
+    "swa": ["gret_swa.hip", "gret_internal.h", "gret_device.h"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gret_prefill_decode_hbm_traffic.json")
 
@@ -86,6 +87,8 @@ def short_kernel_name(name):
 def kernel_group(name):
     if "proj_kernel" in name:
         return "proj"
+    if "swa_prefill" in name or "swa_ring_fill" in name:
+        return "swa"
     if "xattn" in name:
         return "xattn"
     if "output_gate" in name:
@@ -129,7 +132,7 @@ def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
                            "fetch_scale": f_scale, "write_scale": w_scale}}
     fetch = pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = pmc_per_dispatch(write_dir, "WRITE_SIZE")
-    for which in ("prefill", "decode", "decode_gated", "xattn", "epilogue", "proj"):
+    for which in ("prefill", "decode", "decode_gated", "xattn", "epilogue", "proj", "swa"):
         names = sorted(k for k in fetch if kernel_group(k) == which)
         if not names:
             continue
@@ -441,6 +444,95 @@ def bench_projection(gret, dev, B=1, N=524288, D=3072, H=24, dk=128, reps=10, se
     return res
 
 
+def bench_swa(gret, dev, B=1, H=24, N=524288, d=128, W=1024, Bd=256, reps=10, seed=9009,
+              cpu_seconds=0.0, decode=True):
+    """Sliding-window-attention Self-Decoder: prefill of the prefill workload's
+    shape (24 heads of 128, window 1024, q, k, v ~ N(0, 1) bf16 drawn on the
+    device) with the ring fill, and decode steps of 256 sequences over full
+    rings of 1024 positions."""
+    import torch
+
+    g = torch.Generator(device=dev).manual_seed(seed)
+    q = torch.randn((B, H, N, d), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((B, H, N, d), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((B, H, N, d), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    rk = torch.empty((B, H, W, d), dtype=torch.bfloat16, device=dev)
+    rv = torch.empty_like(rk)
+    stream = torch.cuda.current_stream()
+
+    def timed(f, n):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms = timed(lambda: gret.gret_swa_prefill(q, k, v, W, out=out, k_ring=rk, v_ring=rv), reps)
+    keys = B * H * (W * (W + 1) // 2 + (N - W) * W)  # (query, key) pairs inside the windows
+    flops = 4 * d * keys
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {"prefill": {"workload": "swa_prefill_b%d_h%d_n%d_d%d_w%d" % (B, H, N, d, W),
+                       "ms_per_call": ms, "tokens_per_s": B * N / (ms * 1e-3),
+                       "roofline": {"kernel": "swa_prefill_kernel + swa_ring_fill_kernel",
+                                    "bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
+                                    "traffic": recorded_traffic("swa"),
+                                    "algorithmic_flops_per_launch": flops,
+                                    "algorithmic_bytes_per_launch": 4 * B * H * N * d * 2}}}
+    if cpu_seconds > 0:
+        import oracle
+
+        n_cpu = 2048
+        qh = q[:1, :1, :n_cpu].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        kh = k[:1, :1, :n_cpu].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        vh = v[:1, :1, :n_cpu].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.time()
+        calls = 0
+        while time.time() - t0 < cpu_seconds:
+            oracle.oracle_swa_prefill_f64(qh, kh, vh, W)
+            calls += 1
+        dt = time.time() - t0
+        res["prefill"]["cpu_baseline"] = {
+            "value": calls * n_cpu / dt, "unit": "token-heads/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": "one head, first %d positions, %d calls in %.1f s (fp64)" % (n_cpu, calls, dt)}
+    del q, k, v, out, rk, rv
+    torch.cuda.empty_cache()
+    if not decode:
+        return res
+
+    rk = torch.randn((Bd, H, W, d), generator=g, device=dev).to(torch.bfloat16)
+    rv = torch.randn((Bd, H, W, d), generator=g, device=dev).to(torch.bfloat16)
+    qd = torch.randn((Bd, H, d), generator=g, device=dev).to(torch.bfloat16)
+    kn = torch.randn((Bd, H, d), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((Bd, H, d), generator=g, device=dev).to(torch.bfloat16)
+    pos = torch.full((Bd,), 4 * W + 7, dtype=torch.int32, device=dev)
+    od = torch.empty_like(qd)
+    ws = torch.empty(gret.gret_swa_decode_workspace_bytes(Bd, H, H, W, d), dtype=torch.uint8,
+                     device=dev)
+    us = 1000.0 * timed(lambda: gret.gret_swa_decode_step(qd, kn, vn, rk, rv, pos, out=od,
+                                                          workspace=ws), 50)
+    nbytes = 2 * Bd * H * W * d * 2 + 2 * Bd * H * d * 2 * 2
+    achieved = nbytes / (us * 1e-6) / 1e9
+    res["decode"] = {"workload": "swa_decode_b%d_h%d_d%d_w%d" % (Bd, H, d, W),
+                     "us_per_step": us, "steps_per_s": 1e6 / us,
+                     "roofline": {"kernel": "swa_append_kernel + xattn_split_kernel + "
+                                            "xattn_combine_kernel", "bound": "hbm",
+                                  "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                                  "algorithmic_bytes_per_launch": nbytes}}
+    del rk, rv, qd, kn, vn, od, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode(gret, dev, steps_total, reps, warmup_reps):
     import torch
 
@@ -540,10 +632,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=DEFAULT_CHUNK)
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "xattn", "proj"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "xattn", "proj", "swa"], default=None)
     ap.add_argument("--decode-reps", type=int, default=1)
     ap.add_argument("--sweep", action="store_true",
                     help="also time chunk 64/128/256 on the 32K and 512K workloads (stderr)")
+    ap.add_argument("--no-swa-decode", action="store_true",
+                    help="skip the sliding-window decode timing (it runs on the cross-attention "
+                         "kernels, whose counter runs should see only the cross-attention calls)")
     ap.add_argument("--skip-gated", action="store_true",
                     help="skip the gated (output epilogue) prefill and decode timings")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -661,6 +756,22 @@ def main():
             result.update({"value": pj["tokens_per_s"], "unit": "tokens/s",
                            "ms_per_step": pj["ms_per_call"],
                            "config": {"workload": pj["workload"]}, "roofline": pj["roofline"]})
+    if args.only in (None, "swa"):
+        sw = bench_swa(gret, dev, cpu_seconds=0.0 if args.skip_cpu else 3.0,
+                       decode=not args.no_swa_decode)
+        result["swa"] = sw
+        log("swa prefill: %.3f ms/call, %.0f TFLOP/s (%.1f%% of bf16 peak)" % (
+            sw["prefill"]["ms_per_call"], sw["prefill"]["roofline"]["achieved"],
+            100 * sw["prefill"]["roofline"]["frac"]))
+        if "decode" in sw:
+            log("swa decode: %.1f us/step, %.0f GB/s (%.1f%%)" % (
+                sw["decode"]["us_per_step"], sw["decode"]["roofline"]["achieved"],
+                100 * sw["decode"]["roofline"]["frac"]))
+        if args.only == "swa":
+            result.update({"value": sw["prefill"]["tokens_per_s"], "unit": "tokens/s",
+                           "ms_per_step": sw["prefill"]["ms_per_call"],
+                           "config": {"workload": sw["prefill"]["workload"]},
+                           "roofline": sw["prefill"]["roofline"]})
     if args.only in (None, "decode"):
         dec, dd = bench_decode(gret, dev, CONFIGS[5]["decode_steps"], args.decode_reps, 1)
         if not args.skip_cpu:

@@ -33,6 +33,7 @@ constexpr int kSWaves = 8;
 constexpr int kSThreads = 64 * kSWaves;
 constexpr int kSQ = 32 * kSWaves;  // queries per workgroup
 constexpr int kSK = 64;            // keys per LDS stage
+constexpr int kSStages = 3;        // LDS stages (3 or 4), filled kSStages - 1 blocks ahead
 constexpr int kXcds = 8;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -137,7 +138,7 @@ __device__ inline void dma_stage(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc
     for (int i = 0; i < c::PER_WAVE; ++i) dma_block<D, true>(vr, vt, w * c::PER_WAVE + i, key0);
 }
 
-// The three key/value stages in LDS (file scope, so that every helper names
+// The key/value stages in LDS (file scope, so that every helper names
 // the object it touches and the compiler can tell the stages apart when it
 // orders LDS reads after the direct loads into other stages); sized for d = 128.
 __shared__ __attribute__((aligned(1024))) bf16_t swa_k0[kSK * 128];
@@ -146,17 +147,21 @@ __shared__ __attribute__((aligned(1024))) bf16_t swa_k1[kSK * 128];
 __shared__ __attribute__((aligned(1024))) bf16_t swa_v1[kSK * 128];
 __shared__ __attribute__((aligned(1024))) bf16_t swa_k2[kSK * 128];
 __shared__ __attribute__((aligned(1024))) bf16_t swa_v2[kSK * 128];
+__shared__ __attribute__((aligned(1024))) bf16_t swa_k3[kSK * 128];
+__shared__ __attribute__((aligned(1024))) bf16_t swa_v3[kSK * 128];
 template <int X>
 __device__ inline bf16_t* swa_kst() {
     if constexpr (X == 0) return swa_k0;
     if constexpr (X == 1) return swa_k1;
-    return swa_k2;
+    if constexpr (X == 2) return swa_k2;
+    return swa_k3;
 }
 template <int X>
 __device__ inline bf16_t* swa_vst() {
     if constexpr (X == 0) return swa_v0;
     if constexpr (X == 1) return swa_v1;
-    return swa_v2;
+    if constexpr (X == 2) return swa_v2;
+    return swa_v3;
 }
 
 struct SwaParams {
@@ -168,6 +173,10 @@ struct SwaParams {
     int G, q_tiles;
     float scale_log2;  // scale * log2(e)
 };
+
+// 2^x with the hardware instruction (results below 2^-126 flush to 0, which
+// for softmax weights is below the bf16 resolution of the output anyway).
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Running softmax state and output of one wavefront's 32 queries.
 template <int D>
@@ -186,14 +195,26 @@ __device__ inline void swa_block(const bf16_t* kt, const bf16_t* vt, const bf16x
     const int li = lane & 31, hh = lane >> 5;
     f32x16 s[2];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[half][r] = 0.0f;
+    // the two halves are independent accumulation chains: interleave them,
+    // with the LDS reads of K two k-steps ahead of the products
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < c::KS; ++ks)
+    for (int ks = 0; ks < c::KS; ++ks)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
             s[half] = mfma32(lds_read8(kt + soff<D, false>(32 * half + li, 16 * ks + 8 * hh)),
                              qf[ks], s[half]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int g = 0; g < c::KS - 2; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
     // s[half][r] = q[qi] . k[key0 + 32 half + 8 (r / 4) + 4 hh + r % 4]
     if (need_mask) {
 #pragma unroll
@@ -214,7 +235,7 @@ __device__ inline void swa_block(const bf16_t* kt, const bf16_t* vt, const bf16x
     // while a query has seen no admitted key yet its maximum is -inf: subtract
     // 0 instead, so masked scores give exactly 0 and nothing is NaN
     const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
-    const float corr = exp2f((st.m - m_ref) * cl);
+    const float corr = fast_exp2((st.m - m_ref) * cl);
     const float mc = m_ref * cl;
     bf16x8 pb[2][2];
     float psum = 0.0f;
@@ -222,7 +243,7 @@ __device__ inline void swa_block(const bf16_t* kt, const bf16_t* vt, const bf16x
     for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float pr = exp2f(fmaf(s[half][r], cl, -mc));
+            const float pr = fast_exp2(fmaf(s[half][r], cl, -mc));
             psum += pr;
             pb[half][r >> 3][r & 7] = to_bf16(pr);
         }
@@ -253,22 +274,35 @@ __device__ inline void swa_block(const bf16_t* kt, const bf16_t* vt, const bf16x
         }
 }
 
-// One pipeline step over the block i of n (stage X of three): wait for its
-// loads, refill the stage read two steps ago with block i + 2, compute.
+// Waits until this wavefront's loads of a block have landed while those of
+// `later` (0 .. kSStages - 2) further blocks stay in flight.
+template <int D>
+__device__ inline void wait_blocks(int later) {
+    constexpr int M = SCfg<D>::DMA;
+    if (later >= 2) {
+        wait_vm<2 * M>();
+    } else if (later == 1) {
+        wait_vm<M>();
+    } else {
+        wait_vm<0>();
+    }
+}
+
+// One pipeline step over the block i of n (stage X of kSStages): wait for its
+// loads, refill the stage read one step ago with block i + kSStages - 1,
+// compute.
 template <int D, int X>
 __device__ inline void swa_step(int i, int n,
                                 int64_t kb0, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                 const bf16x8 (&qf)[SCfg<D>::KS], int64_t qi, int64_t qw0,
                                 int64_t W, float cl, SwaAcc<D>& st) {
-    using c = SCfg<D>;
-    if (n - 1 - i >= 1)
-        wait_vm<c::DMA>();
-    else
-        wait_vm<0>();
+    constexpr int AHEAD = kSStages - 1;
+    const int later = n - 1 - i < AHEAD - 1 ? n - 1 - i : AHEAD - 1;
+    wait_blocks<D>(later);
     lds_barrier();
-    if (i + 2 < n)
-        dma_stage<D>(kr, vr, swa_kst<(X + 2) % 3>(), swa_vst<(X + 2) % 3>(),
-                     static_cast<uint32_t>((kb0 + i + 2) * kSK));
+    if (i + AHEAD < n)
+        dma_stage<D>(kr, vr, swa_kst<(X + AHEAD) % kSStages>(), swa_vst<(X + AHEAD) % kSStages>(),
+                     static_cast<uint32_t>((kb0 + i + AHEAD) * kSK));
     const int64_t key0 = (kb0 + i) * kSK;
     // this wavefront's queries qw0 .. qw0 + 31 see keys qw0 - W + 1 .. qw0 + 31
     const bool active = key0 + kSK > qw0 - W + 1 && key0 <= qw0 + 31;
@@ -323,14 +357,20 @@ __global__ __launch_bounds__(kSThreads) void swa_prefill_kernel(SwaParams p) {
 
     dma_stage<D>(kr, vr, swa_kst<0>(), swa_vst<0>(), static_cast<uint32_t>(kb0 * kSK));
     if (n > 1) dma_stage<D>(kr, vr, swa_kst<1>(), swa_vst<1>(), static_cast<uint32_t>((kb0 + 1) * kSK));
+    if (kSStages > 3 && n > 2)
+        dma_stage<D>(kr, vr, swa_kst<2>(), swa_vst<2>(), static_cast<uint32_t>((kb0 + 2) * kSK));
+#define GRET_SWA_STEP(X) swa_step<D, X>(i + X, n, kb0, kr, vr, qf, qi, qw0, W, cl, st)
     int i = 0;
-    for (; i + 3 <= n; i += 3) {
-        swa_step<D, 0>(i, n, kb0, kr, vr, qf, qi, qw0, W, cl, st);
-        swa_step<D, 1>(i + 1, n, kb0, kr, vr, qf, qi, qw0, W, cl, st);
-        swa_step<D, 2>(i + 2, n, kb0, kr, vr, qf, qi, qw0, W, cl, st);
+    for (; i + kSStages <= n; i += kSStages) {
+        GRET_SWA_STEP(0);
+        GRET_SWA_STEP(1);
+        GRET_SWA_STEP(2);
+        if constexpr (kSStages > 3) GRET_SWA_STEP(3);
     }
-    if (i < n) swa_step<D, 0>(i, n, kb0, kr, vr, qf, qi, qw0, W, cl, st);
-    if (i + 1 < n) swa_step<D, 1>(i + 1, n, kb0, kr, vr, qf, qi, qw0, W, cl, st);
+    if (i < n) GRET_SWA_STEP(0);
+    if (i + 1 < n) GRET_SWA_STEP(1);
+    if (kSStages > 3 && i + 2 < n) GRET_SWA_STEP(2);
+#undef GRET_SWA_STEP
 
     if (qi >= N) return;
     const float l = st.l + __shfl_xor(st.l, 32);
