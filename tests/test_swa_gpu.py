@@ -128,7 +128,6 @@ def test_swa_prefill_full_size_sampled(gret):
                                      rng.integers(0, N, 120)]))
     worst = 0.0
     for h in (0, 17):
-        lo = 0
         for i in rows:
             j0 = max(0, int(i) - W + 1)
             qs = to_host(q[0, h, i:i + 1].contiguous())[None, None]
@@ -140,7 +139,6 @@ def test_swa_prefill_full_size_sampled(gret):
             r = oracle_swa_prefill_f64(qq, ks, vs, W)[0, 0, -1]
             got = to_host(out[0, h, i].contiguous())
             worst = max(worst, eps(got, r))
-            lo += 1
     say("   sampled %d rows x 2 heads: worst eps_out=%.3e" % (len(rows), worst))
     assert worst <= TOL
     del q, k, v, out

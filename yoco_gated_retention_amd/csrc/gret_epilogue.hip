@@ -13,8 +13,11 @@
 // 64 consecutive rows of one head, so the head's affine for a lane's channels
 // is loaded once; each lane owns one 16-byte piece of a row, a row is spread
 // over dv * sizeof(T) / 16 adjacent lanes, and a wavefront issues the loads of
-// all its rows before any arithmetic. Mean and variance (two passes over
-// registers, fp32) are reduced with cross-lane exchanges inside a row's lanes.
+// all its rows before any arithmetic. Rows past N are handled by range-checked
+// buffer accesses (loads read 0, stores are dropped), so no branch sits between
+// the loads and they all stay in flight together. Mean and variance (two
+// passes over registers, fp32) are reduced with cross-lane exchanges inside a
+// row's lanes.
 #include <hip/hip_runtime.h>
 
 #include "gret_device.h"
@@ -26,6 +29,17 @@ namespace {
 constexpr int kEpiThreads = 256;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, gfx9-family data format
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
+}
+__device__ inline i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, i32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
 
 // swish(x) = x * sigmoid(x), with the hardware reciprocal (about 1 ulp).
 __device__ inline float swish(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
@@ -35,27 +49,27 @@ struct Piece;  // one 16-byte piece of a row, widened to fp32
 template <>
 struct Piece<float> {
     static constexpr int N = 4;
-    static __device__ inline void load(const float* p, float (&x)[N]) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+    static __device__ inline void unpack(i32x4 raw, float (&x)[N]) {
+        const f32x4 v = __builtin_bit_cast(f32x4, raw);
         x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
     }
-    static __device__ inline void store(float* p, const float (&x)[N]) {
-        *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+    static __device__ inline i32x4 pack(const float (&x)[N]) {
+        return __builtin_bit_cast(i32x4, f32x4{x[0], x[1], x[2], x[3]});
     }
 };
 template <>
 struct Piece<bf16_t> {
     static constexpr int N = 8;
-    static __device__ inline void load(const bf16_t* p, float (&x)[N]) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+    static __device__ inline void unpack(i32x4 raw, float (&x)[N]) {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, raw);
 #pragma unroll
         for (int i = 0; i < N; ++i) x[i] = from_bf16(v[i]);
     }
-    static __device__ inline void store(bf16_t* p, const float (&x)[N]) {
+    static __device__ inline i32x4 pack(const float (&x)[N]) {
         bf16x8 v;
 #pragma unroll
         for (int i = 0; i < N; ++i) v[i] = to_bf16(x[i]);
-        *reinterpret_cast<bf16x8*>(p) = v;
+        return __builtin_bit_cast(i32x4, v);
     }
 };
 
@@ -94,42 +108,42 @@ __global__ __launch_bounds__(kEpiThreads) void output_gate_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c0 = (lane % LPR) * VPL;
     const int64_t h = bh % H;
+    // this workgroup's rows of the head, as one range-checked buffer each
+    const int64_t rows = N - n0 < kRowsPerGroup ? N - n0 : kRowsPerGroup;
+    const uint32_t bytes = static_cast<uint32_t>(rows * DV * sizeof(T));
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + (bh * N + n0) * DV, bytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gate + (bh * N + n0) * DV, bytes);
+    i32x4 xr[STEPS], gr[STEPS];
+    uint32_t off[STEPS];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        const int r = (s * WAVES + wave) * RPW + lane / LPR;
+        off[s] = static_cast<uint32_t>((r * DV + c0) * sizeof(T));
+        xr[s] = buf_load16(ro, off[s]);
+        gr[s] = buf_load16(rg, off[s]);
+    }
     float w[VPL], b[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         w[i] = weight ? weight[h * DV + c0 + i] : 1.0f;
         b[i] = bias ? bias[h * DV + c0 + i] : 0.0f;
     }
-    float x[STEPS][VPL], g[STEPS][VPL];
-    bool ok[STEPS];
-    int64_t off[STEPS];
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
-        const int64_t n = n0 + (s * WAVES + wave) * RPW + lane / LPR;
-        ok[s] = n < N;  // the same for all lanes of a row
-        off[s] = (bh * N + n) * DV + c0;
-        if (ok[s]) {
-            Piece<T>::load(out + off[s], x[s]);
-            Piece<T>::load(gate + off[s], g[s]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) x[s][i] = g[s][i] = 0.0f;
-        }
-    }
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
+        float x[VPL], g[VPL];
+        Piece<T>::unpack(xr[s], x);
+        Piece<T>::unpack(gr[s], g);
         float sum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) sum += x[s][i];
+        for (int i = 0; i < VPL; ++i) sum += x[i];
         const float mean = group_sum<LPR>(sum) * (1.0f / DV);
         float sq = 0.0f;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) sq += (x[s][i] - mean) * (x[s][i] - mean);
+        for (int i = 0; i < VPL; ++i) sq += (x[i] - mean) * (x[i] - mean);
         const float rstd = rsqrtf(group_sum<LPR>(sq) * (1.0f / DV) + eps);
 #pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            x[s][i] = swish(g[s][i]) * ((x[s][i] - mean) * rstd * w[i] + b[i]);
-        if (ok[s]) Piece<T>::store(out + off[s], x[s]);
+        for (int i = 0; i < VPL; ++i) x[i] = swish(g[i]) * ((x[i] - mean) * rstd * w[i] + b[i]);
+        buf_store16(ro, off[s], Piece<T>::pack(x));
     }
 }
 
