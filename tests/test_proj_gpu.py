@@ -130,3 +130,31 @@ def test_projection_full_size_sampled(gret):
     assert e_k <= TOL_K and e_l <= TOL_L
     del x, k, lg
     torch.cuda.empty_cache()
+
+
+def test_projection_feeds_retention(gret):
+    """The projection's outputs are the retention's key and log-gate inputs:
+    project keys and log-gates on the GPU, run the chunkwise prefill on them,
+    and compare with the oracle projection followed by the oracle recurrence
+    (queries and values drawn directly, as the projection of x by other
+    weights would give)."""
+    import oracle
+    from workloads import f32_to_bf16_bits
+
+    B, N, D, H, dk = 1, 700, 512, 4, 128
+    x, wk, wg = make_projection_inputs(31, B, N, D, H, dk)
+    rng = np.random.default_rng(32)
+    q = f32_to_bf16_bits((rng.standard_normal((B, H, N, dk)) / np.sqrt(dk)).astype(np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((B, H, N, dk)).astype(np.float32))
+    k_dev, lg_dev = gret.gret_head_projection(to_dev(x), to_dev(wk), to_dev(wg),
+                                              key_scale=dk ** -0.5, temperature=16.0)
+    out, st = gret.gret_prefill(to_dev(q), k_dev, to_dev(v), lg_dev, None, chunk=64)
+    torch.cuda.synchronize()
+    oracle.build_oracle(force=False)
+    k_ref, lg_ref = oracle_head_projection_f64(x, wk, wg, key_scale=dk ** -0.5, temperature=16.0)
+    # the retention oracle takes the stored types: keys in bf16, log-gates in fp32
+    k_bits = f32_to_bf16_bits(k_ref.astype(np.float32))
+    o_ref, s_ref, _ = oracle.oracle_prefill_f64(q, k_bits, v, lg_ref.astype(np.float32))
+    e_o, e_s = eps(to_host(out), o_ref), eps(to_host(st), s_ref)
+    say("projection -> prefill: eps_out=%.3e eps_state=%.3e" % (e_o, e_s))
+    assert e_o <= TOL_K and e_s <= TOL_K
