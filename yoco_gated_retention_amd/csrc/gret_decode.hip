@@ -57,17 +57,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const int cg = tid % CG;
     const int rg = tid / CG;
 
-    for (int i = tid; i < DK; i += kDecodeThreads) {
-        s_q[i] = load_as_float(q, head * DK + i);
-        s_k[i] = load_as_float(k, head * DK + i);
-    }
-    const float gamma = __expf(clamp_log_gamma(log_gamma[head], kLogGammaFloor));
-    f32x4 vv;
-    vv[0] = load_as_float(v, head * DV + 4 * cg + 0);
-    vv[1] = load_as_float(v, head * DV + 4 * cg + 1);
-    vv[2] = load_as_float(v, head * DV + 4 * cg + 2);
-    vv[3] = load_as_float(v, head * DV + 4 * cg + 3);
-
+    // The state loads go out first: the token's q, k, v and gate are small and
+    // their latency then overlaps the state's.
     const int64_t base = head * DK * DV;
     f32x4 s[RPT];
     if (state_in) {
@@ -78,6 +69,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     } else {
 #pragma unroll
         for (int r = 0; r < RPT; ++r) s[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float gamma = __expf(clamp_log_gamma(log_gamma[head], kLogGammaFloor));
+    f32x4 vv;
+    vv[0] = load_as_float(v, head * DV + 4 * cg + 0);
+    vv[1] = load_as_float(v, head * DV + 4 * cg + 1);
+    vv[2] = load_as_float(v, head * DV + 4 * cg + 2);
+    vv[3] = load_as_float(v, head * DV + 4 * cg + 3);
+    for (int i = tid; i < DK; i += kDecodeThreads) {
+        s_q[i] = load_as_float(q, head * DK + i);
+        s_k[i] = load_as_float(k, head * DK + i);
     }
     __syncthreads();  // s_q, s_k ready
 
