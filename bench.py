@@ -665,9 +665,9 @@ def main():
                           "calibrate_copy_bytes_written": dst.numel() * 2, "copies": 3}))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads and sequences shard across GPUs without communication; see DESIGN.md). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (heads and "
+              "sequences shard across GPUs without communication, each GPU running these "
+              "kernels on its share). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
