@@ -178,6 +178,10 @@ struct SwaParams {
 // for softmax weights is below the bf16 resolution of the output anyway).
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// How far (log2 units) a score may exceed the softmax reference before the
+// reference moves and the output is rescaled.
+constexpr float kLazyLog2 = 8.0f;
+
 // Running softmax state and output of one wavefront's 32 queries.
 template <int D>
 struct SwaAcc {
@@ -231,11 +235,16 @@ __device__ inline void swa_block(const bf16_t* kt, const bf16_t* vt, const bf16x
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[half][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(st.m, mt);
-    // while a query has seen no admitted key yet its maximum is -inf: subtract
-    // 0 instead, so masked scores give exactly 0 and nothing is NaN
+    // st.m is the reference the weights are taken against, not the running
+    // maximum: it moves only when a score exceeds it by more than kLazyLog2
+    // (in log2 units), so the weights stay <= 2^kLazyLog2 and the output is
+    // rescaled rarely; the final division by l makes the reference cancel.
+    const bool grow = (mt - st.m) * cl > kLazyLog2;
+    const float m_new = grow ? mt : st.m;
+    // while a query has seen no admitted key yet its reference is -inf:
+    // subtract 0 instead, so masked scores give exactly 0 and nothing is NaN
     const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
-    const float corr = fast_exp2((st.m - m_ref) * cl);
+    const float corr = grow ? fast_exp2((st.m - m_ref) * cl) : 1.0f;
     const float mc = m_ref * cl;
     bf16x8 pb[2][2];
     float psum = 0.0f;
