@@ -339,8 +339,11 @@ void proj_kernel(ProjParams p) {
     const uint32_t tt = first + in_group % gm;
     const int ct = static_cast<int>(in_group / gm);
     const int64_t m0 = static_cast<int64_t>(tt) * kPM;
-    if (ct < p.key_tiles)
-        key_tile(p, m0, ct);
+    // the gate column (when there is one) comes first in each group, next to
+    // the first key tiles of the same token tiles, while their x rows are in L2
+    const int kt = p.col_tiles > p.key_tiles ? ct - 1 : ct;
+    if (kt >= 0)
+        key_tile(p, m0, kt);
     else if (p.H <= 32)
         gate_tile<2>(p, m0);
     else if (p.H <= 64)
