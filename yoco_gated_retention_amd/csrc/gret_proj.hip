@@ -38,7 +38,7 @@ constexpr int kPK = 32;         // hidden features per pipeline stage (D: a mult
 constexpr int kPThreads = 256;  // 4 wavefronts: 2 along channels x 2 along tokens
 constexpr int kPWave = 128;     // channels and tokens per wavefront
 constexpr int kPStage = (kPN + kPM) * kPK;  // bf16 per stage: weight rows, then x rows
-constexpr int kPGroupM = 8;     // token tiles per group of the workgroup order
+constexpr int kPGroupM = 6;     // token tiles per group of the workgroup order
 constexpr int kXcds = 8;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
