@@ -143,3 +143,21 @@ def test_swa_prefill_full_size_sampled(gret):
     assert worst <= TOL
     del q, k, v, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("q_scale", [8.0, 30.0])
+def test_swa_prefill_peaked_scores(gret, q_scale):
+    """Scores with standard deviation 8 and 30: the running softmax maximum
+    jumps often and far, so the output rescaling path runs many times (and
+    weights far below the maximum underflow to 0)."""
+    B, Hq, Hkv, N, d, W = 1, 2, 1, 1500, 128, 512
+    q, k, v = make_attention_inputs(int(q_scale), B, Hq, Hkv, N, d)
+    from workloads import f32_to_bf16_bits
+
+    q = f32_to_bf16_bits(bf16_bits_to_f32(q) * np.float32(q_scale))
+    say("swa_prefill peaked scores q_scale=%g" % q_scale)
+    out = gret.gret_swa_prefill(to_dev(q), to_dev(k), to_dev(v), W)
+    torch.cuda.synchronize()
+    e = eps(to_host(out), oracle_swa_prefill_f64(q, k, v, W))
+    say("   eps_out=%.3e" % e)
+    assert e <= TOL
