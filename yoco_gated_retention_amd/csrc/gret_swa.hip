@@ -85,8 +85,11 @@ __device__ inline void lds_barrier() {
 // Tile layouts: row-major, the 16-byte chunks of row r permuted by c ^ sw(r).
 // K is read as 16-byte row pieces of 8 consecutive rows (any 8 aligned rows
 // land in 8 different 16-byte slots of a 128-byte bank period); V with the
-// transposing read, 4 consecutive rows x 32 bytes per 16-lane group (the 4
-// rows land in 4 different 32-byte slots).
+// transposing read, 4 consecutive rows x 32 bytes per 16-lane group, the two
+// half-wavefronts 4 rows apart. Measured on the kernel's own addresses (bytes
+// per clock and CU, 128-column tiles): K 227 with its layout; V 163 with
+// sw = 4 (r % 4) + (r / 4) % 4, against 116 with the K/V layout of the
+// chunk-64 prefill, whose rows r and r + 4 share a 32-byte slot pair.
 template <int D>
 __device__ inline int kswz(int r) {
     if constexpr (D == 128) return ((r & 1) << 2) | ((r >> 1) & 3) | (((r >> 3) & 1) << 3);
@@ -94,7 +97,7 @@ __device__ inline int kswz(int r) {
 }
 template <int D>
 __device__ inline int vswz(int r) {
-    if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
     return ((r & 3) << 1) | ((r >> 2) & 1);
 }
 template <int D, bool IS_V>
