@@ -11,12 +11,15 @@ resident in HBM when timing starts.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk C]
                        [--skip-cpu] [--only prefill|decode] [--sweep]
        python bench.py --calibrate-copy
-       python bench.py --summarize-pmc FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+       python bench.py --summarize-pmc FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR [MFMA_DIR]
 
 HBM traffic: the figures recorded in profiles/gret_prefill_decode_hbm_traffic.json (rocprofv3
 FETCH_SIZE / WRITE_SIZE per dispatch, scaled by what the same counters read for
 a plain copy of known size) are reported only while the kernel sources hash to
-the values recorded with them; otherwise traffic is null.
+the values recorded with them; otherwise traffic is null. The matrix-core
+utilisation recorded there (rocprofv3's MfmaUtil: busy cycles of the MFMA
+units over active cycles x SIMDs, per dispatch of the dominant kernel) follows
+the same rule.
 """
 from __future__ import annotations
 
@@ -77,6 +80,22 @@ def recorded_traffic(which):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
+def recorded_mfma(which, kernel):
+    """rocprofv3 MfmaUtil (percent) of the named kernel of an entry point from
+    the committed counter summary, or None (missing, or other sources)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[which]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_sha256(which):
+        return None
+    for name, k in rec.get("kernels", {}).items():
+        if kernel in name and "mfma_util_pct" in k:
+            return k["mfma_util_pct"]
+    return None
+
+
 def short_kernel_name(name):
     name = name.replace("(anonymous namespace)::", "")
     if name.startswith("void "):
@@ -117,10 +136,12 @@ def pmc_per_dispatch(d, counter):
     return {k: (n, tot / n) for k, (n, tot) in acc.items()}
 
 
-def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir, mfma_dir=None):
     """Scales FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by the plain-copy
     calibration and sums them per entry-point call (the prefill is three
-    launches: main, combine, prefix)."""
+    launches: main, combine, prefix). With mfma_dir (a run of MfmaUtil and
+    SQ_INSTS_VALU_MFMA_MOPS_BF16), each kernel also gets its matrix-core
+    utilisation and the bf16 matrix flops the hardware counted."""
     copy_bytes = 1 << 30  # --calibrate-copy: 1 GiB read and 1 GiB written per copy
     cf = [v for k, (n, v) in pmc_per_dispatch(cfetch_dir, "FETCH_SIZE").items() if "copy" in k]
     cw = [v for k, (n, v) in pmc_per_dispatch(cwrite_dir, "WRITE_SIZE").items() if "copy" in k]
@@ -132,6 +153,8 @@ def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
                            "fetch_scale": f_scale, "write_scale": w_scale}}
     fetch = pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = pmc_per_dispatch(write_dir, "WRITE_SIZE")
+    util = pmc_per_dispatch(mfma_dir, "MfmaUtil") if mfma_dir else {}
+    mops = pmc_per_dispatch(mfma_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16") if mfma_dir else {}
     for which in ("prefill", "decode", "decode_gated", "xattn", "epilogue", "proj", "swa"):
         names = sorted(k for k in fetch if kernel_group(k) == which)
         if not names:
@@ -143,6 +166,11 @@ def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
                 "write_kib": write.get(k, (0, float("nan")))[1],
                 "fetch_bytes": fetch[k][1] * 1024.0 * f_scale,
                 "write_bytes": write.get(k, (0, 0.0))[1] * 1024.0 * w_scale}
+            if k in util:
+                kern[short_kernel_name(k)]["mfma_util_pct"] = util[k][1]
+            if k in mops:
+                # one MOPS unit is 512 flops
+                kern[short_kernel_name(k)]["mfma_bf16_flops"] = mops[k][1] * 512.0
         out[which] = {"sources_sha256": sources_sha256(which), "kernels": kern,
                       "fetch_bytes": sum(x["fetch_bytes"] for x in kern.values()),
                       "write_bytes": sum(x["write_bytes"] for x in kern.values())}
@@ -416,6 +444,7 @@ def bench_projection(gret, dev, B=1, N=524288, D=3072, H=24, dk=128, reps=10, se
            "roofline": {"kernel": "proj_kernel", "bound": "mfma", "achieved": tf,
                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": tf / BF16_PEAK_TFLOPS, "traffic": recorded_traffic("proj"),
+                        "mfma_busy_pct": recorded_mfma("proj", "proj_kernel"),
                         "algorithmic_flops_per_launch": flops,
                         "algorithmic_bytes_per_launch": nbytes}}
     if cpu_seconds > 0:
@@ -484,6 +513,7 @@ def bench_swa(gret, dev, B=1, H=24, N=524288, d=128, W=1024, Bd=256, reps=10, se
                                     "bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
                                     "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
                                     "traffic": recorded_traffic("swa"),
+                                    "mfma_busy_pct": recorded_mfma("swa", "swa_prefill_kernel"),
                                     "algorithmic_flops_per_launch": flops,
                                     "algorithmic_bytes_per_launch": 4 * B * H * N * d * 2}}}
     if cpu_seconds > 0:
@@ -643,14 +673,17 @@ def main():
                     help="skip the gated (output epilogue) prefill and decode timings")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of each CPU-oracle baseline")
-    ap.add_argument("--summarize-pmc", nargs=4, metavar="DIR", default=None,
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR", default=None,
                     help="print HBM traffic per call from rocprofv3 --pmc output directories "
-                         "(FETCH_SIZE run, WRITE_SIZE run, and the two --calibrate-copy runs)")
+                         "(FETCH_SIZE run, WRITE_SIZE run, the two --calibrate-copy runs, and "
+                         "optionally a MfmaUtil + SQ_INSTS_VALU_MFMA_MOPS_BF16 run)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB (x3) to calibrate the HBM "
                          "traffic counters")
     args = ap.parse_args()
     if args.summarize_pmc:
+        if len(args.summarize_pmc) not in (4, 5):
+            ap.error("--summarize-pmc takes 4 or 5 directories")
         summarize_pmc(*args.summarize_pmc)
         return
     if args.calibrate_copy:
@@ -705,7 +738,8 @@ def main():
                          "traffic": recorded_traffic("prefill"),
                          "algorithmic_bytes_per_launch": nbytes,
                          "mfma_tflops": flops / (ms * 1e-3) / 1e12,
-                         "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+                         "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                         "mfma_busy_pct": recorded_mfma("prefill", "prefill_main_c64_kernel")},
         })
         log("prefill chunk=%d: %.3f ms/step, %.3e tokens/s, %.0f GB/s (%.1f%% of HBM peak)" % (
             args.chunk, ms, result["value"], achieved, 100 * achieved / HBM_PEAK_GBS))
