@@ -569,7 +569,7 @@ def bench_decode(gret, dev, steps_total, reps, warmup_reps):
     from workloads import make_decode_inputs
 
     t0 = time.time()
-    d = make_decode_inputs(5, steps=steps_total)
+    d = make_decode_inputs("decode_b256", steps=steps_total)
     log("decode inputs generated in %.1f s" % (time.time() - t0))
     B, H, dk, dv = d["B"], d["H"], d["dk"], d["dv"]
     state = to_dev(d["state"], dev)
@@ -719,9 +719,9 @@ def main():
 
     d3 = None
     if args.only in (None, "prefill"):
-        cfg = CONFIGS[3]
+        cfg = CONFIGS["prefill_512k"]
         t0 = time.time()
-        d3 = make_prefill_inputs(3)
+        d3 = make_prefill_inputs("prefill_512k")
         log("prefill inputs generated in %.1f s" % (time.time() - t0))
         ms = time_prefill(gret, d3, args.chunk, args.steps, args.warmup, dev)
         B, H, N, dk, dv = 1, cfg["H"], cfg["N"], cfg["dk"], cfg["dv"]
@@ -744,8 +744,8 @@ def main():
         log("prefill chunk=%d: %.3f ms/step, %.3e tokens/s, %.0f GB/s (%.1f%% of HBM peak)" % (
             args.chunk, ms, result["value"], achieved, 100 * achieved / HBM_PEAK_GBS))
         if args.sweep:
-            for cid in (2, 3):
-                dd = d3 if cid == 3 else make_prefill_inputs(2)
+            for cid in ("prefill_32k", "prefill_512k"):
+                dd = d3 if cid == "prefill_512k" else make_prefill_inputs(cid)
                 c = CONFIGS[cid]
                 for ch in (64, 128, 256):
                     m = time_prefill(gret, dd, ch, max(3, args.steps // 2), 2, dev)
@@ -807,7 +807,7 @@ def main():
                            "config": {"workload": sw["prefill"]["workload"]},
                            "roofline": sw["prefill"]["roofline"]})
     if args.only in (None, "decode"):
-        dec, dd = bench_decode(gret, dev, CONFIGS[5]["decode_steps"], args.decode_reps, 1)
+        dec, dd = bench_decode(gret, dev, CONFIGS["decode_b256"]["decode_steps"], args.decode_reps, 1)
         if not args.skip_cpu:
             dec["cpu_baseline"] = cpu_decode_baseline(dd, args.cpu_seconds)
         result["decode"] = dec

@@ -103,7 +103,7 @@ def test_prefill_gated_short_rows(gret):
 
 
 def test_prefill_gated_32k_all_heads(gret):
-    d = make_prefill_inputs(2)
+    d = make_prefill_inputs("prefill_32k")
     rng = np.random.default_rng(2002)
     H, N, dv = d["q"].shape[1], d["q"].shape[2], d["v"].shape[3]
     gate = f32_to_bf16_bits((2.0 * rng.standard_normal((1, H, N, dv))).astype(np.float32))
@@ -147,7 +147,7 @@ def test_decode_gated_small(gret, dtype, dk, dv):
 
 
 def test_decode_gated_full_batch_sampled(gret):
-    d = make_decode_inputs(5, steps=20)
+    d = make_decode_inputs("decode_b256", steps=20)
     B, H, dv = d["B"], d["H"], d["dv"]
     rng = np.random.default_rng(5005)
     w = (1.0 + 0.2 * rng.standard_normal((H, dv))).astype(np.float32)

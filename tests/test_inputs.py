@@ -19,18 +19,18 @@ def test_bf16_rounding_matches_torch():
 
 
 def test_prefill_inputs_are_deterministic_and_per_head():
-    a = make_prefill_inputs(2, N=256, H=3)
-    b = make_prefill_inputs(2, N=256, H=3)
+    a = make_prefill_inputs("prefill_32k", N=256, H=3)
+    b = make_prefill_inputs("prefill_32k", N=256, H=3)
     for key in ("q", "k", "v", "log_gamma"):
         np.testing.assert_array_equal(a[key], b[key])
     # one stream per head: drawing a subset reproduces the same head
-    c = make_prefill_inputs(2, N=256, H=3, heads=[1])
+    c = make_prefill_inputs("prefill_32k", N=256, H=3, heads=[1])
     np.testing.assert_array_equal(c["q"][0, 1], a["q"][0, 1])
     assert not c["q"][0, 0].any()
 
 
 def test_prefill_value_statistics():
-    d = make_prefill_inputs(3, N=65536, H=2)
+    d = make_prefill_inputs("prefill_512k", N=65536, H=2)
     lg = d["log_gamma"]
     assert lg.dtype == np.float32 and np.all(lg <= 0)
     sharp = lg == LN_SHARP_GAMMA
@@ -44,13 +44,14 @@ def test_prefill_value_statistics():
 
 
 def test_config_table():
-    assert CONFIGS[1]["dtype"] == "f32" and CONFIGS[1]["chunks"] == (64,)
-    assert CONFIGS[3]["N"] == 524288 and CONFIGS[4]["N"] == 1048576
-    assert CONFIGS[4]["s0_std"] == 0.1 and CONFIGS[3]["sharp_frac"] == 0.01
+    assert CONFIGS["tiny_f32"]["dtype"] == "f32" and CONFIGS["tiny_f32"]["chunks"] == (64,)
+    assert CONFIGS["prefill_512k"]["N"] == 524288 and CONFIGS["prefill_1m"]["N"] == 1048576
+    assert CONFIGS["prefill_1m"]["s0_std"] == 0.1 and CONFIGS["prefill_512k"]["sharp_frac"] == 0.01
+    assert len({c["seed"] for c in CONFIGS.values()}) == len(CONFIGS)
 
 
 def test_decode_inputs_shapes():
-    d = make_decode_inputs(5, B=2, H=3, steps=4)
+    d = make_decode_inputs("decode_b256", B=2, H=3, steps=4)
     assert d["state"].shape == (2, 3, 128, 128)
     assert d["q"].shape == (4, 2, 3, 128) and d["q"].dtype == np.uint16
     assert abs(d["state"].std() - 0.1) < 0.005

@@ -255,7 +255,7 @@ def test_three_b_state_size_arithmetic():
     # dk x dv and does not depend on the sequence length.
     from workloads import CONFIGS
 
-    for cid in (2, 3, 4, 5):
-        c = CONFIGS[cid]
+    for name in ("prefill_32k", "prefill_512k", "prefill_1m", "decode_b256"):
+        c = CONFIGS[name]
         assert (c["H"], c["dk"], c["dv"]) == (24, 128, 128)
     assert 13 * 24 * 128 * 128 * 2 == int(9.75 * 2 ** 20)

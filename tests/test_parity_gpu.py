@@ -85,12 +85,12 @@ def small_inputs(B, H, N, dk, dv, dtype="bf16", seed=5, s0=True, lg_mode="gate")
 
 # ---------------------------------------------------------------- fp32 path
 
-def test_cfg1_fp32_prefill_then_16_decode_steps(gret):
-    d = make_prefill_inputs(1)
-    out, st, o_ref, s_ref = check_prefill(gret, d, 64, TOL_F32, label="cfg1")
+def test_tiny_f32_prefill_then_16_decode_steps(gret):
+    d = make_prefill_inputs("tiny_f32")
+    out, st, o_ref, s_ref = check_prefill(gret, d, 64, TOL_F32, label="tiny_f32")
     state = to_dev(st)
     s64 = s_ref.copy()
-    for t in range(CONFIGS[1]["decode_steps"]):
+    for t in range(CONFIGS["tiny_f32"]["decode_steps"]):
         o = gret.gret_decode_step(to_dev(d["dec_q"][t]), to_dev(d["dec_k"][t]),
                                   to_dev(d["dec_v"][t]), to_dev(d["dec_log_gamma"][t]), state)
         torch.cuda.synchronize()
@@ -202,9 +202,9 @@ def test_bf16_bitwise_deterministic(gret):
 # ------------------------------------------------- full-size workloads (configs)
 
 @pytest.mark.parametrize("chunk", [64, 128, 256])
-def test_cfg2_full(gret, chunk):
-    d = make_prefill_inputs(2)
-    say("cfg2 chunk=%d" % chunk)
+def test_prefill_32k_full(gret, chunk):
+    d = make_prefill_inputs("prefill_32k")
+    say("prefill_32k chunk=%d" % chunk)
     out, st = gpu_prefill(gret, d, chunk)
     _, s_ref, stats = oracle.oracle_prefill_f64(d["q"], d["k"], d["v"], d["log_gamma"],
                                                 want_out=False, compare=out)
@@ -216,10 +216,10 @@ def test_cfg2_full(gret, chunk):
 SAMPLE_HEADS = (0, 11, 23)
 
 
-def _sampled_check(gret, cfg_id, chunk, first_chunk=False):
-    d = make_prefill_inputs(cfg_id)
+def _sampled_check(gret, workload, chunk, first_chunk=False):
+    d = make_prefill_inputs(workload)
     s0 = d["s0"]
-    say("cfg%d N=%d chunk=%d (oracle on heads %s)" % (cfg_id, d["N"], chunk, SAMPLE_HEADS))
+    say("%s N=%d chunk=%d (oracle on heads %s)" % (workload, d["N"], chunk, SAMPLE_HEADS))
     out, st = gpu_prefill(gret, d, chunk, s0)
     hs = list(SAMPLE_HEADS)
 
@@ -244,12 +244,12 @@ def _sampled_check(gret, cfg_id, chunk, first_chunk=False):
         assert e_f <= TOL_BF16
 
 
-def test_cfg3_full_sampled_heads(gret):
-    _sampled_check(gret, 3, 64)
+def test_prefill_512k_sampled_heads(gret):
+    _sampled_check(gret, "prefill_512k", 64)
 
 
-def test_cfg4_full_sampled_heads(gret):
-    _sampled_check(gret, 4, 64, first_chunk=True)
+def test_prefill_1m_sampled_heads(gret):
+    _sampled_check(gret, "prefill_1m", 64, first_chunk=True)
 
 
 # ------------------------------------------------------------------ decode
@@ -278,13 +278,13 @@ def test_decode_small(gret, dtype, dk, dv):
     assert eps(to_host(o), o_r) <= tol and eps(to_host(so), z) <= tol
 
 
-def test_cfg5_decode_1000_steps_sampled(gret):
-    cfg = CONFIGS[5]
+def test_decode_b256_1000_steps_sampled(gret):
+    cfg = CONFIGS["decode_b256"]
     B, H, steps = cfg["B"], cfg["H"], cfg["decode_steps"]
     rng = np.random.default_rng(5)
     heads = sorted(rng.choice(B * H, 48, replace=False).tolist())
-    say("cfg5 decode B=%d H=%d steps=%d, oracle on %d heads" % (B, H, steps, len(heads)))
-    d = make_decode_inputs(5, heads=heads)
+    say("decode_b256 B=%d H=%d steps=%d, oracle on %d heads" % (B, H, steps, len(heads)))
+    d = make_decode_inputs("decode_b256", heads=heads)
     state = to_dev(d["state"])
     q, k, v, lg = (to_dev(d[key]) for key in ("q", "k", "v", "log_gamma"))
     hidx = torch.tensor(heads, device="cuda")

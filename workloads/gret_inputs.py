@@ -7,11 +7,11 @@ Retention" with the temperature 16 of section "单 token Decode 的实现骨架"
 already scaled by d^(-1/2), at the 3B model's mixer width of 24 heads x 128
 (section "用 3B 配置手算一遍").
 
-Recipe (one PCG64 stream per (batch, head), seed = 1000 + config id, child i of
-SeedSequence(seed) for flattened head i):
+Recipe (one PCG64 stream per (batch, head), seed = the workload's "seed", child i
+of SeedSequence(seed) for flattened head i):
   draw order per head: u[N] -> q[N,dk] -> k[N,dk] -> v[N,dv] -> sharp mask[N]
-  (only when the config forces sharp forgetting) -> S0[dk,dv] (only when the
-  config has an initial state) -> decode tokens (u, q, k, v per step).
+  (only when the workload forces sharp forgetting) -> S0[dk,dv] (only when the
+  workload has an initial state) -> decode tokens (u, q, k, v per step).
   Normals are float32 ziggurat draws; q and k are scaled by dk^-0.5 in float32
   (variance 1/dk), v is unit normal; S0 is 0.1 * normal (variance 0.01).
   log_gamma = float32(-softplus(-u) / 16) evaluated in float64, i.e. the log of
@@ -28,18 +28,23 @@ import numpy as np
 
 LN_SHARP_GAMMA = np.float32(np.log(0.1))
 
-# id -> workload description. "chunks" lists the chunk sizes exercised.
+# The workloads, by name. "chunks" lists the chunk sizes exercised; "seed" is
+# the root of each workload's seeded streams (one stream per head).
 CONFIGS = {
-    1: dict(name="tiny_f32_b1h2_n512_d64", B=1, H=2, N=512, dk=64, dv=64, dtype="f32",
-            chunks=(64,), s0_std=0.0, sharp_frac=0.0, decode_steps=16),
-    2: dict(name="prefill_b1h24_n32768_d128", B=1, H=24, N=32768, dk=128, dv=128,
-            dtype="bf16", chunks=(64, 128, 256), s0_std=0.0, sharp_frac=0.0, decode_steps=0),
-    3: dict(name="prefill_b1h24_n524288_d128_sharp1pct", B=1, H=24, N=524288, dk=128, dv=128,
-            dtype="bf16", chunks=(64, 128, 256), s0_std=0.0, sharp_frac=0.01, decode_steps=0),
-    4: dict(name="prefill_b1h24_n1048576_d128_s0", B=1, H=24, N=1048576, dk=128, dv=128,
-            dtype="bf16", chunks=(64, 128, 256), s0_std=0.1, sharp_frac=0.0, decode_steps=0),
-    5: dict(name="decode_b256h24_d128_1000steps", B=256, H=24, N=0, dk=128, dv=128,
-            dtype="bf16", chunks=(), s0_std=0.1, sharp_frac=0.0, decode_steps=1000),
+    "tiny_f32": dict(name="tiny_f32_b1h2_n512_d64", B=1, H=2, N=512, dk=64, dv=64, dtype="f32",
+                     chunks=(64,), s0_std=0.0, sharp_frac=0.0, decode_steps=16, seed=1001),
+    "prefill_32k": dict(name="prefill_b1h24_n32768_d128", B=1, H=24, N=32768, dk=128, dv=128,
+                        dtype="bf16", chunks=(64, 128, 256), s0_std=0.0, sharp_frac=0.0,
+                        decode_steps=0, seed=1002),
+    "prefill_512k": dict(name="prefill_b1h24_n524288_d128_sharp1pct", B=1, H=24, N=524288,
+                         dk=128, dv=128, dtype="bf16", chunks=(64, 128, 256), s0_std=0.0,
+                         sharp_frac=0.01, decode_steps=0, seed=1003),
+    "prefill_1m": dict(name="prefill_b1h24_n1048576_d128_s0", B=1, H=24, N=1048576, dk=128,
+                       dv=128, dtype="bf16", chunks=(64, 128, 256), s0_std=0.1, sharp_frac=0.0,
+                       decode_steps=0, seed=1004),
+    "decode_b256": dict(name="decode_b256h24_d128_1000steps", B=256, H=24, N=0, dk=128, dv=128,
+                        dtype="bf16", chunks=(), s0_std=0.1, sharp_frac=0.0, decode_steps=1000,
+                        seed=1005),
 }
 
 
@@ -79,7 +84,7 @@ def _draw_token_block(rng, n, dk, dv, dtype):
     return _log_gamma(u), _store(q, dtype), _store(k, dtype), _store(v, dtype)
 
 
-def prefill_head(cfg: dict, cfg_id: int, head: int, N: int | None = None, dtype: str | None = None,
+def prefill_head(cfg: dict, head: int, N: int | None = None, dtype: str | None = None,
                  decode_steps: int | None = None):
     """Draw one flattened head's inputs (see the module recipe).
 
@@ -90,7 +95,7 @@ def prefill_head(cfg: dict, cfg_id: int, head: int, N: int | None = None, dtype:
     dtype = cfg["dtype"] if dtype is None else dtype
     steps = cfg["decode_steps"] if decode_steps is None else decode_steps
     dk, dv = cfg["dk"], cfg["dv"]
-    rng = _rng(1000 + cfg_id, head)
+    rng = _rng(cfg["seed"], head)
     lg, q, k, v = _draw_token_block(rng, N, dk, dv, dtype)
     if cfg["sharp_frac"] > 0.0:
         mask = rng.random(N) < cfg["sharp_frac"]
@@ -116,7 +121,7 @@ def _workers(n):
     return max(1, min(n, cpus, 16))
 
 
-def make_prefill_inputs(cfg_id: int, *, N: int | None = None, B: int | None = None,
+def make_prefill_inputs(workload: str, *, N: int | None = None, B: int | None = None,
                         H: int | None = None, dtype: str | None = None,
                         decode_steps: int | None = None, heads=None):
     """Draw a whole prefill workload (optionally at a reduced N / B / H).
@@ -126,7 +131,7 @@ def make_prefill_inputs(cfg_id: int, *, N: int | None = None, B: int | None = No
     Returns dict(q, k, v [B,H,N,d] (uint16 bf16 bits or float32), log_gamma
     [B,H,N] float32, s0 [B,H,dk,dv] float32 or None, dec_* arrays [steps,B,H,...]).
     """
-    cfg = CONFIGS[cfg_id]
+    cfg = CONFIGS[workload]
     B = cfg["B"] if B is None else B
     H = cfg["H"] if H is None else H
     N = cfg["N"] if N is None else N
@@ -147,7 +152,7 @@ def make_prefill_inputs(cfg_id: int, *, N: int | None = None, B: int | None = No
 
     def one(x):
         b, h = divmod(x, H)
-        d = prefill_head(cfg, cfg_id, x, N=N, dtype=dtype, decode_steps=steps)
+        d = prefill_head(cfg, x, N=N, dtype=dtype, decode_steps=steps)
         q[b, h], k[b, h], v[b, h], lg[b, h] = d["q"], d["k"], d["v"], d["log_gamma"]
         if s0 is not None:
             s0[b, h] = d["s0"]
@@ -160,7 +165,7 @@ def make_prefill_inputs(cfg_id: int, *, N: int | None = None, B: int | None = No
                 dec_v=dvv, B=B, H=H, N=N, dk=dk, dv=dv, dtype=dtype)
 
 
-def make_decode_inputs(cfg_id: int = 5, *, B: int | None = None, H: int | None = None,
+def make_decode_inputs(workload: str = "decode_b256", *, B: int | None = None, H: int | None = None,
                        steps: int | None = None, heads=None):
     """Batched decode workload: initial state [B,H,dk,dv] (std cfg s0_std) and a
     pool of ``steps`` single tokens per (sequence, head).
@@ -169,7 +174,7 @@ def make_decode_inputs(cfg_id: int = 5, *, B: int | None = None, H: int | None =
     Returns dict(state [B,H,dk,dv] f32, log_gamma [steps,B,H] f32,
     q,k [steps,B,H,dk], v [steps,B,H,dv] (uint16 bf16 bits or float32)).
     """
-    cfg = CONFIGS[cfg_id]
+    cfg = CONFIGS[workload]
     B = cfg["B"] if B is None else B
     H = cfg["H"] if H is None else H
     steps = cfg["decode_steps"] if steps is None else steps
@@ -184,7 +189,7 @@ def make_decode_inputs(cfg_id: int = 5, *, B: int | None = None, H: int | None =
 
     def one(x):
         b, h = divmod(x, H)
-        rng = _rng(1000 + cfg_id, x)
+        rng = _rng(cfg["seed"], x)
         state[b, h] = rng.standard_normal((dk, dv), dtype=np.float32) * np.float32(cfg["s0_std"])
         a, qq, kk, vv = _draw_token_block(rng, steps, dk, dv, dtype)
         lg[:, b, h], q[:, b, h], k[:, b, h], v[:, b, h] = a, qq, kk, vv
