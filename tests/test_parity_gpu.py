@@ -165,6 +165,42 @@ def test_bf16_split_prefill_then_decode(gret):
     assert eps(to_host(state), s64) <= TOL_BF16
 
 
+def _random_cases(n, seed):
+    """Seeded random shapes: batch and head counts that split sequences across
+    segment ranges, ragged N, every head-dim pair and chunk size, each gate
+    regime, with or without an initial state."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = "f32" if rng.random() < 0.25 else "bf16"
+        modes = ["gate", "mixed"] if dtype == "f32" else ["gate", "gate", "mixed", "one", "zero"]
+        cases.append((dtype, int(rng.integers(1, 4)), int(rng.integers(1, 8)),
+                      int(rng.integers(1, 2500)), int(rng.choice([64, 128])),
+                      int(rng.choice([64, 128])), int(rng.choice([64, 128, 256])),
+                      str(rng.choice(modes)), bool(rng.integers(0, 2)), 7000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(16, 20261203),
+                         ids=lambda c: "%s_B%dH%dN%d_dk%d_dv%d_c%d_%s_s0%d" % c[:9])
+def test_random_shapes_prefill_then_decode(gret, case):
+    dtype, B, H, N, dk, dv, chunk, lg_mode, s0, seed = case
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    d, S0 = small_inputs(B, H, N, dk, dv, dtype=dtype, seed=seed, s0=s0, lg_mode=lg_mode)
+    _, st, _, s_ref = check_prefill(gret, d, chunk, tol, S0, label="random")
+    # three decode steps from the GPU's final state, against the oracle's
+    state = to_dev(st)
+    s64 = s_ref.copy()
+    dd, _ = small_inputs(B, H, 3, dk, dv, dtype=dtype, seed=seed + 500, s0=False, lg_mode=lg_mode)
+    for t in range(3):
+        args = [np.ascontiguousarray(dd[key][:, :, t]) for key in ("q", "k", "v", "log_gamma")]
+        o = gret.gret_decode_step(*(to_dev(a) for a in args), state)
+        torch.cuda.synchronize()
+        o_r = oracle.oracle_decode_f64(*args, s64)
+        assert eps(to_host(o), o_r) <= tol, ("decode step", t)
+    assert eps(to_host(state), s64) <= tol
+
+
 def test_bf16_in_place_state_and_no_state_out(gret):
     d, S0 = small_inputs(2, 2, 900, 128, 128, seed=41)
     q, k, v, lg = (to_dev(d[key]) for key in ("q", "k", "v", "log_gamma"))
