@@ -66,6 +66,25 @@ def test_swa_prefill_and_ring(gret, B, Hq, Hkv, N, d, W):
     np.testing.assert_array_equal(bf16_bits_to_f32(to_host(rv)), wv)
 
 
+def _random_cases(n, seed):
+    """Seeded random shapes: batch, grouped heads, ragged prompts and windows
+    from 1 to beyond the prompt, both d."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Hkv = int(rng.integers(1, 4))
+        N = int(rng.integers(1, 2500))
+        W = int(rng.integers(1, 3000))
+        cases.append((int(rng.integers(1, 3)), Hkv * int(rng.integers(1, 4)), Hkv, N,
+                      int(rng.choice([64, 128])), W))
+    return cases
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,W", _random_cases(10, 20261205))
+def test_swa_prefill_and_ring_random(gret, B, Hq, Hkv, N, d, W):
+    test_swa_prefill_and_ring(gret, B, Hq, Hkv, N, d, W)
+
+
 def test_swa_prefill_without_rings(gret):
     q, k, v = make_attention_inputs(3, 1, 2, 2, 600, 128)
     out = gret.gret_swa_prefill(to_dev(q), to_dev(k), to_dev(v), 300)

@@ -74,6 +74,31 @@ def test_scale_argument(gret):
     check(gret, 2, 6, 2, 900, 64, scale=0.4, seed=9, label="scale")
 
 
+def _random_cases(n, seed):
+    """Seeded random shapes: group sizes up to the supported 16, batches with
+    per-sequence lengths from 1 to L, short and long caches, both d, and an
+    explicit scale on some."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B, Hkv = int(rng.integers(1, 5)), int(rng.integers(1, 4))
+        G = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+        L = int(rng.integers(1, 6000))
+        lengths = None
+        if rng.random() < 0.5:
+            lengths = [int(x) for x in rng.integers(1, L + 1, B)]
+        scale = float(rng.uniform(0.02, 0.3)) if rng.random() < 0.3 else None
+        cases.append((B, Hkv * G, Hkv, L, int(rng.choice([64, 128])), lengths, scale, 9000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(12, 20261204),
+                         ids=lambda c: "B%dHq%dHkv%dL%d_d%d" % c[:5])
+def test_random_shapes(gret, case):
+    B, Hq, Hkv, L, d, lengths, scale, seed = case
+    check(gret, B, Hq, Hkv, L, d, lengths=lengths, scale=scale, seed=seed, label="random")
+
+
 def test_deterministic(gret):
     q, k, v = inputs(1, 24, 8, 2048, 128, 10)
     a = gret.gret_cross_attention_decode(to_dev(q), to_dev(k), to_dev(v))
