@@ -68,6 +68,28 @@ def test_projection_with_gate(gret, B, N, D, H, dk):
     check(gret, B, N, D, H, dk, seed=B * 1000 + N + D + H + dk)
 
 
+def _random_cases(n, seed):
+    """Seeded random shapes: batch, ragged sequences, hidden sizes that are
+    multiples of 128, dk multiples of 16 up to 256, gate heads up to 64, with
+    and without the gate, and other scales and temperatures."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        cases.append((int(rng.integers(1, 4)), int(rng.integers(1, 1200)),
+                      128 * int(rng.integers(1, 9)), int(rng.integers(1, 65)),
+                      16 * int(rng.integers(1, 17)), bool(rng.random() < 0.75),
+                      float(rng.uniform(0.05, 1.0)), float(rng.choice([1.0, 4.0, 16.0])),
+                      11000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(12, 20261206),
+                         ids=lambda c: "B%dN%dD%dH%d_dk%d_gate%d" % c[:6])
+def test_projection_random_shapes(gret, case):
+    B, N, D, H, dk, gate, scale, tau, seed = case
+    check(gret, B, N, D, H, dk, gate=gate, scale=scale, tau=tau, seed=seed)
+
+
 def test_projection_gate_heads_beyond_one_wavefront(gret):
     # 100 gate heads: channels 64..99 of the gate tile fall to a second wavefront
     check(gret, 1, 520, 256, 100, 16, seed=77)
