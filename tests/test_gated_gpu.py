@@ -96,6 +96,31 @@ def test_prefill_gated_f32(gret, chunk):
     check_prefill_gated(gret, d, S0, gate, w, b, 1e-5, chunk, TOL_F32, "f32")
 
 
+def _random_cases(n, seed):
+    """Seeded random shapes for the gated prefill: dtype, batch, heads, ragged
+    N, dims, chunk, with or without the affine and the initial state, and
+    GroupNorm eps from tiny to large."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = "f32" if rng.random() < 0.25 else "bf16"
+        cases.append((dtype, int(rng.integers(1, 4)), int(rng.integers(1, 7)),
+                      int(rng.integers(1, 2000)), int(rng.choice([64, 128])),
+                      int(rng.choice([64, 128])), int(rng.choice([64, 128, 256])),
+                      bool(rng.integers(0, 2)), bool(rng.integers(0, 2)),
+                      float(rng.choice([1e-6, 1e-5, 1e-2, 0.5])), 13000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(10, 20261207),
+                         ids=lambda c: "%s_B%dH%dN%d_dk%d_dv%d_c%d" % c[:7])
+def test_prefill_gated_random_shapes(gret, case):
+    dtype, B, H, N, dk, dv, chunk, affine, s0, norm_eps, seed = case
+    d, S0, gate, w, b = seeded_inputs(B, H, N, dk, dv, dtype, seed=seed, s0=s0)
+    check_prefill_gated(gret, d, S0, gate, w if affine else None, b if affine else None,
+                        norm_eps, chunk, TOL_F32 if dtype == "f32" else TOL_BF16, "random")
+
+
 def test_prefill_gated_short_rows(gret):
     for N in (1, 63, 65):
         d, S0, gate, w, b = seeded_inputs(1, 3, N, 128, 128, "bf16", seed=N)
