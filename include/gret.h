@@ -65,7 +65,9 @@ typedef enum {
 typedef enum {
     GRET_OK = 0,
     GRET_ERR_NULL = 1,        /* a required pointer is NULL                   */
-    GRET_ERR_SHAPE = 2,       /* B, H or N < 1, or sizes overflow             */
+    GRET_ERR_SHAPE = 2,       /* B, H or N < 1, sizes overflow, or a launch
+                                 would need more than 2^31 - 1 workgroups
+                                 (limits stated per entry point)             */
     GRET_ERR_UNSUPPORTED = 3, /* dk, dv, chunk or dtype outside the set below,
                                  or a tensor pointer not 16-byte aligned      */
     GRET_ERR_ALIAS = 4,       /* out overlaps an input, or states overlap
@@ -112,7 +114,8 @@ int gret_prefill_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, in
  *   B, H, N             >= 1; N need not be a multiple of chunk (the tail chunk
  *                       is masked and state_out is exactly S_{N-1}); with
  *                       dtype BF16, N <= 2^23 (one head's rows are addressed
- *                       with 32-bit offsets), else GRET_ERR_SHAPE
+ *                       with 32-bit offsets), else GRET_ERR_SHAPE;
+ *                       B*H <= 2^27 - 1 (also for the decode step)
  *   dk, dv              64 or 128
  *   chunk               64, 128 or 256 -- the chunk length of the chunkwise form
  *   dtype               gret_dtype_t of q, k, v, out
@@ -202,7 +205,8 @@ int gret_decode_step_gated(const void* q, const void* k, const void* v, const fl
  *              accesses stay inside the caches)
  *   scale      finite (usually d^-1/2), else GRET_ERR_VALUE
  *   dtype      GRET_DTYPE_BF16 only (else GRET_ERR_UNSUPPORTED)
- *   d          64 or 128;  Hq a multiple of Hkv with Hq / Hkv <= 16;  L <= 2^23
+ *   d          64 or 128;  Hq a multiple of Hkv with Hq / Hkv <= 16;  L <= 2^23;
+ *              B*Hq <= 2^30 - 1
  *   workspace  at least gret_cross_attention_workspace_bytes(...) bytes,
  *              256-byte aligned (per-range partial results); calls that share
  *              a workspace must be ordered on one stream
@@ -264,7 +268,9 @@ int gret_head_projection(const void* x, const void* w_key, const void* w_gamma, 
  *   k_ring, v_ring  [B,Hkv,window,d] bf16, or both NULL: when given, slot
  *                p mod window receives position p for the last min(N, window)
  *                positions (other slots are left as they are)
- *   N, window    1 .. 2^23;  d 64 or 128;  Hq a multiple of Hkv
+ *   N, window    1 .. 2^23;  d 64 or 128;  Hq a multiple of Hkv;  B*Hq*max(N,
+ *                window)*d <= 2^50 and each launch <= 2^31 - 1 workgroups
+ *                (B*Hq*ceil(N/256) for the attention)
  *   scale        finite (usually d^-1/2), else GRET_ERR_VALUE
  *   dtype        GRET_DTYPE_BF16 only (else GRET_ERR_UNSUPPORTED)
  * out and the rings must not overlap each other or an input (GRET_ERR_ALIAS).

@@ -252,6 +252,18 @@ def test_swa_validation(lib):
     assert swa_dec(lib, scale=float("nan")) == VALUE
 
 
+def test_launch_size_limits(lib):
+    # Shapes whose launches would need more than 2^31 - 1 workgroups, or whose
+    # sizes pass 2^50 elements, are rejected before anything is enqueued.
+    assert prefill(lib, B=1 << 27, H=1, N=1) == SHAPE          # combine: 16 per head
+    assert prefill(lib, B=(1 << 27) - 1, H=1, N=1, ws=None) == WORKSPACE  # the limit itself
+    assert decode(lib, B=1 << 27, H=1) == SHAPE
+    assert prefill_gated(lib, B=1, H=1 << 20, N=1 << 20) == SHAPE  # epilogue: 2^34 row groups
+    assert xattn(lib, B=1 << 28, Hq=4, Hkv=4, L=1) == SHAPE     # combine: B*Hq = 2^30
+    assert swa_pre(lib, B=1 << 17, Hq=1, Hkv=1, N=1 << 23, d=64) == SHAPE  # 2^32 query tiles
+    assert swa_pre(lib, B=1 << 30, Hq=1 << 10, Hkv=1 << 10, N=1 << 23) == SHAPE  # > 2^50
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(gret, "_lib", None)
     monkeypatch.setattr(gret, "LIB_PATH", "/nonexistent/libgret.so")

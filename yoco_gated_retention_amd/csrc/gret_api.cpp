@@ -44,6 +44,10 @@ int check_common(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int dt
     if (B < 1 || H < 1 || N < 1) return GRET_ERR_SHAPE;
     if (B > kMaxElems || H > kMaxElems / B || N > kMaxElems / (B * H)) return GRET_ERR_SHAPE;
     if (B * H * N > kMaxElems / 128) return GRET_ERR_SHAPE;
+    // Launches that scale with B*H: the decode step (B*H workgroups), the fp32
+    // prefill (B*H*dv/32) and the bf16 prefill's combine (B*H*dk*dv/1024, at
+    // most 16 per head); the bf16 prefill's other launches have <= 1024.
+    if (B * H > gret::kMaxGridGroups / 16) return GRET_ERR_SHAPE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GRET_ERR_UNSUPPORTED;
     return GRET_OK;
 }
@@ -130,6 +134,7 @@ int prefill_impl(const void* q, const void* k, const void* v, const float* log_g
                             &sgw, &sgb);
         if (st != GRET_OK) return st;
     }
+    if (epi && gret::output_gate_groups(BHN, N) > gret::kMaxGridGroups) return GRET_ERR_SHAPE;
     const size_t need = workspace_need(B, H, N, dk, dv, chunk, dtype);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
         return GRET_ERR_WORKSPACE;
@@ -256,7 +261,9 @@ const char* gret_status_string(int status) {
     switch (status) {
         case GRET_OK: return "GRET_OK: success";
         case GRET_ERR_NULL: return "GRET_ERR_NULL: a required pointer is NULL";
-        case GRET_ERR_SHAPE: return "GRET_ERR_SHAPE: B, H or N is < 1 or the sizes overflow";
+        case GRET_ERR_SHAPE:
+            return "GRET_ERR_SHAPE: B, H or N is < 1, the sizes overflow, or a launch would need "
+                   "more than 2^31 - 1 workgroups";
         case GRET_ERR_UNSUPPORTED:
             return "GRET_ERR_UNSUPPORTED: dk/dv not in {64,128}, chunk not in {64,128,256}, "
                    "unknown dtype, or a tensor pointer not 16-byte aligned";
@@ -335,6 +342,9 @@ int check_xattn(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d) {
     if (B < 1 || Hq < 1 || Hkv < 1 || L < 1) return GRET_ERR_SHAPE;
     if (B > kMaxElems || Hq > kMaxElems / B || L > (int64_t(1) << 23)) return GRET_ERR_SHAPE;
     if (B * Hkv > kMaxElems / L / 128 || B * Hq > kMaxElems / 128) return GRET_ERR_SHAPE;
+    // the combine launch has B*Hq workgroups, the split launch at most
+    // B*Hkv + 1023 (about 1024 in all, or one per sequence and KV head)
+    if (B * Hq > gret::kMaxGridGroups / 2) return GRET_ERR_SHAPE;
     if (d != 64 && d != 128) return GRET_ERR_UNSUPPORTED;
     if (Hq % Hkv != 0 || Hq / Hkv > 16) return GRET_ERR_UNSUPPORTED;
     return GRET_OK;
@@ -464,6 +474,11 @@ int gret_swa_prefill(const void* q, const void* k, const void* v, void* out, voi
     int st = check_swa(B, Hq, Hkv, d, window, dtype);
     if (st != GRET_OK) return st;
     if (N < 1 || N > kSwaMaxN) return GRET_ERR_SHAPE;
+    const int64_t span_rows = N > window ? N : window;  // positions of q/k/v/out, of the rings
+    if (B * Hq > kMaxElems / (span_rows * d)) return GRET_ERR_SHAPE;
+    if (gret::swa_prefill_groups(B, Hq, Hkv, N, d, window, k_ring != nullptr) >
+        gret::kMaxGridGroups)
+        return GRET_ERR_SHAPE;
     if (!isfinite(scale)) return GRET_ERR_VALUE;
     for (const void* p : {q, k, v, (const void*)out, (const void*)k_ring, (const void*)v_ring})
         if (p && !aligned(p, 16)) return GRET_ERR_UNSUPPORTED;

@@ -150,9 +150,8 @@ __global__ __launch_bounds__(kEpiThreads) void output_gate_kernel(
 template <typename T>
 hipError_t launch_t(const EpilogueArgs& a) {
     const int64_t per_head = (a.N + kRowsPerGroup - 1) / kRowsPerGroup;
-    const int64_t heads = a.rows / a.N;
-    const int64_t blocks = heads * per_head;
-    if (blocks < 1 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const int64_t blocks = output_gate_groups(a.rows, a.N);
+    if (blocks < 1 || blocks > kMaxGridGroups) return hipErrorInvalidValue;
     T* out = static_cast<T*>(a.out);
     const T* gate = static_cast<const T*>(a.epi.gate);
     if (a.dv == 64)
@@ -169,6 +168,10 @@ hipError_t launch_t(const EpilogueArgs& a) {
 }
 
 }  // namespace
+
+int64_t output_gate_groups(int64_t rows, int64_t N) {
+    return rows / N * ((N + kRowsPerGroup - 1) / kRowsPerGroup);
+}
 
 hipError_t launch_output_gate_f32(const EpilogueArgs& a) { return launch_t<float>(a); }
 hipError_t launch_output_gate_bf16(const EpilogueArgs& a) { return launch_t<bf16_t>(a); }

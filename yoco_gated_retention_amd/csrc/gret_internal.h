@@ -16,6 +16,10 @@ constexpr float kLogGammaFloor = -80.0f;
 // exp(B) falls below the smallest normal fp32 number (exp(-87.34)).
 constexpr float kSurvivalDropLog = -88.0f;
 
+// Workgroups one launch may have (a single grid dimension). The C ABI checks
+// every launch of a call against it before anything is enqueued.
+constexpr int64_t kMaxGridGroups = 0x7fffffff;
+
 struct PrefillArgs {
     const void* q;
     const void* k;
@@ -102,6 +106,8 @@ hipError_t launch_xattn_decode(const XAttnArgs& a);
 
 hipError_t launch_output_gate_f32(const EpilogueArgs& a);
 hipError_t launch_output_gate_bf16(const EpilogueArgs& a);
+// Workgroups of the epilogue launch for `rows` rows of heads of N positions.
+int64_t output_gate_groups(int64_t rows, int64_t N);
 
 // Key and log-gate projection (gret_proj.hip): x [B*N, D] bf16, weights as
 // rows; keys head-major [B,H,N,dk] bf16 times key_scale, log-gates [B,H,N].
@@ -131,6 +137,9 @@ struct SwaArgs {
     hipStream_t stream;
 };
 hipError_t launch_swa_prefill(const SwaArgs& a);
+// Workgroups of the larger of the prefill's two launches (attention, ring fill).
+int64_t swa_prefill_groups(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                           int64_t window, bool ring);
 struct SwaDecodeArgs {
     const void* k_new;  // [B,Hkv,d]
     const void* v_new;

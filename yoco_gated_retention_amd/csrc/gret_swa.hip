@@ -437,6 +437,22 @@ __global__ __launch_bounds__(64) void swa_append_kernel(
 
 }  // namespace
 
+namespace {
+// Workgroups per KV head of the ring fill: the last min(N, window) rows, d / 8
+// 16-byte pieces each, one piece per thread.
+int64_t ring_fill_groups_per_head(int64_t N, int64_t d, int64_t window) {
+    const int64_t keep = N < window ? N : window;
+    return (keep * (d / 8) + kCopyThreads - 1) / kCopyThreads;
+}
+}  // namespace
+
+int64_t swa_prefill_groups(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                           int64_t window, bool ring) {
+    const int64_t attn = B * Hq * ((N + kSQ - 1) / kSQ);
+    const int64_t fill = ring ? B * Hkv * ring_fill_groups_per_head(N, d, window) : 0;
+    return attn > fill ? attn : fill;
+}
+
 hipError_t launch_swa_prefill(const SwaArgs& a) {
     SwaParams p;
     p.q = static_cast<const bf16_t*>(a.q);
@@ -451,7 +467,8 @@ hipError_t launch_swa_prefill(const SwaArgs& a) {
     p.G = static_cast<int>(a.Hq / a.Hkv);
     const int64_t qt = (a.N + kSQ - 1) / kSQ;
     const int64_t blocks = a.B * a.Hq * qt;
-    if (blocks < 1 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const int64_t most = swa_prefill_groups(a.B, a.Hq, a.Hkv, a.N, a.d, a.window, a.k_ring != nullptr);
+    if (blocks < 1 || most > kMaxGridGroups) return hipErrorInvalidValue;
     p.q_tiles = static_cast<int>(qt);
     p.scale_log2 = a.scale * 1.4426950408889634f;
     if (a.d == 128)
@@ -464,8 +481,7 @@ hipError_t launch_swa_prefill(const SwaArgs& a) {
         return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.k_ring) return e;
-    const int64_t keep = a.N < a.window ? a.N : a.window;
-    const int64_t per_head = (keep * (a.d / 8) + kCopyThreads - 1) / kCopyThreads;
+    const int64_t per_head = ring_fill_groups_per_head(a.N, a.d, a.window);
     hipLaunchKernelGGL(swa_ring_fill_kernel, dim3(static_cast<unsigned>(a.B * a.Hkv * per_head)),
                        dim3(kCopyThreads), 0, a.stream, p.k, p.v,
                        static_cast<bf16_t*>(a.k_ring), static_cast<bf16_t*>(a.v_ring), a.N,
