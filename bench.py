@@ -9,7 +9,8 @@ reported in the same JSON line. Inputs are seeded synthetic data already
 resident in HBM when timing starts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk C]
-                       [--skip-cpu] [--only prefill|decode] [--sweep]
+                       [--skip-cpu] [--skip-peaks] [--skip-gated]
+                       [--only prefill|decode|xattn|proj|swa]
        python bench.py --calibrate-copy
        python bench.py --summarize-pmc FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR [MFMA_DIR]
 
@@ -198,12 +199,31 @@ def decode_algorithmic(B, H, dk, dv):
     return nbytes, flops
 
 
-def cpu_threads():
+def host_cpus():
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return os.cpu_count() or 1
+
+
+def cpu_threads():
+    """Oracle threads: the cores this process may run on, at most 16 (the
+    host share of one GPU)."""
+    return max(1, min(host_cpus(), 16))
+
+
+def cpu_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count(), "cpus_available": host_cpus(),
+            "oracle_threads": cpu_threads()}
 
 
 def to_dev(a, dev):
@@ -214,74 +234,103 @@ def to_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def time_prefill(gret, d, chunk, steps, warmup, dev):
+def time_calls(fn, steps, warmup):
+    """Runs fn warmup times, synchronises, then times `steps` back-to-back calls
+    on the current stream with one HIP event before each call and one after the
+    last. Returns (mean ms over the block, median ms of the calls, per-call ms)."""
     import torch
 
-    q, k, v = to_dev(d["q"], dev), to_dev(d["k"], dev), to_dev(d["v"], dev)
-    lg = to_dev(d["log_gamma"], dev)
-    si = None if d.get("s0") is None else to_dev(d["s0"], dev)
-    B, H, N, dk = d["q"].shape
-    dv = d["v"].shape[3]
-    out = torch.empty((B, H, N, dv), dtype=torch.bfloat16, device=dev)
-    so = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    need = gret.gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, 1)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     for _ in range(warmup):
-        gret.gret_prefill(q, k, v, lg, si, chunk=chunk, out=out, state_out=so, workspace=ws)
+        fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        gret.gret_prefill(q, k, v, lg, si, chunk=chunk, out=out, state_out=so, workspace=ws)
-    e1.record(stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        ev[i].record(stream)
+        fn()
+    ev[steps].record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    del q, k, v, lg, out, so, ws
-    torch.cuda.empty_cache()
-    return ms
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / steps, float(np.median(per)), per
 
 
-def time_prefill_gated(gret, d, chunk, steps, warmup, dev, seed=3003):
-    """Plain and gated prefill on the same inputs (gate: seeded normal, bf16;
-    affine: seeded, fp32). The difference of the two call times is the output
-    epilogue's pass."""
+class DevicePrefill:
+    """One prefill workload resident on the device, with its output, state and
+    workspace allocated once (outside any timed region)."""
+
+    def __init__(self, gret, d, dev, log_gamma=None):
+        import torch
+
+        self.gret = gret
+        self.q, self.k, self.v = to_dev(d["q"], dev), to_dev(d["k"], dev), to_dev(d["v"], dev)
+        self.lg = to_dev(d["log_gamma"] if log_gamma is None else log_gamma, dev)
+        self.si = None if d.get("s0") is None else to_dev(d["s0"], dev)
+        self.B, self.H, self.N, self.dk = d["q"].shape
+        self.dv = d["v"].shape[3]
+        dt = self.q.dtype
+        self.out = torch.empty((self.B, self.H, self.N, self.dv), dtype=dt, device=dev)
+        self.so = torch.empty((self.B, self.H, self.dk, self.dv), dtype=torch.float32, device=dev)
+        self.code = 1 if dt == torch.bfloat16 else 0
+        self.ws = {}
+
+    def set_log_gamma(self, lg, dev):
+        self.lg = to_dev(lg, dev)
+
+    def workspace(self, chunk):
+        import torch
+
+        if chunk not in self.ws:
+            need = self.gret.gret_prefill_workspace_bytes(self.B, self.H, self.N, self.dk, self.dv,
+                                                          chunk, self.code)
+            self.ws[chunk] = torch.empty(max(need, 1), dtype=torch.uint8, device=self.q.device)
+        return self.ws[chunk]
+
+    def call(self, chunk):
+        ws = self.workspace(chunk)
+        return lambda: self.gret.gret_prefill(self.q, self.k, self.v, self.lg, self.si, chunk=chunk,
+                                              out=self.out, state_out=self.so, workspace=ws)
+
+    def time(self, chunk, steps, warmup):
+        return time_calls(self.call(chunk), steps, warmup)
+
+    def free(self):
+        import torch
+
+        self.q = self.k = self.v = self.lg = self.si = self.out = self.so = None
+        self.ws = {}
+        torch.cuda.empty_cache()
+
+
+def prefill_roofline(B, H, N, dk, dv, chunk, state_in, ms, kernel, measured_gbs=None):
+    nbytes, flops = prefill_algorithmic(B, H, N, dk, dv, chunk, state_in)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    r = {"kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
+         "algorithmic_flops_per_launch": flops, "mfma_tflops": flops / (ms * 1e-3) / 1e12,
+         "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    if measured_gbs:
+        r["peak_measured"] = measured_gbs
+        r["frac_measured"] = achieved / measured_gbs
+    return r
+
+
+def time_prefill_gated(dp, chunk, steps, warmup, dev, seed=3003):
+    """Plain and gated prefill on the same resident inputs (gate: seeded normal,
+    bf16; affine: seeded, fp32). The difference of the two call times is the
+    output epilogue's pass."""
     import torch
 
-    q, k, v = to_dev(d["q"], dev), to_dev(d["k"], dev), to_dev(d["v"], dev)
-    lg = to_dev(d["log_gamma"], dev)
-    B, H, N, dk = d["q"].shape
-    dv = d["v"].shape[3]
+    B, H, N, dv = dp.B, dp.H, dp.N, dp.dv
     g = torch.Generator(device=dev).manual_seed(seed)
     gate = (2.0 * torch.randn((B, H, N, dv), generator=g, device=dev)).to(torch.bfloat16)
     w = 1.0 + 0.2 * torch.randn((H, dv), generator=g, device=dev)
     b = 0.2 * torch.randn((H, dv), generator=g, device=dev)
-    out = torch.empty((B, H, N, dv), dtype=torch.bfloat16, device=dev)
-    so = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(gret.gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, 1), 1),
-                     dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def timed(f):
-        for _ in range(warmup):
-            f()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            f()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
-
-    plain = timed(lambda: gret.gret_prefill(q, k, v, lg, None, chunk=chunk, out=out, state_out=so,
-                                            workspace=ws))
-    gated = timed(lambda: gret.gret_prefill_gated(q, k, v, lg, gate, norm_weight=w, norm_bias=b,
-                                                  chunk=chunk, out=out, state_out=so,
-                                                  workspace=ws))
-    del q, k, v, lg, gate, out, so, ws
+    ws = dp.workspace(chunk)
+    plain = time_calls(dp.call(chunk), steps, warmup)[1]
+    gated = time_calls(lambda: dp.gret.gret_prefill_gated(
+        dp.q, dp.k, dp.v, dp.lg, gate, state_in=dp.si, norm_weight=w, norm_bias=b, chunk=chunk,
+        out=dp.out, state_out=dp.so, workspace=ws), steps, warmup)[1]
+    del gate, w, b
     torch.cuda.empty_cache()
     rows = B * H * N
     epi_bytes = rows * dv * 2 * 3 + 2 * H * dv * 4
@@ -289,11 +338,85 @@ def time_prefill_gated(gret, d, chunk, steps, warmup, dev, seed=3003):
     achieved = epi_bytes / (epi_ms * 1e-3) / 1e9 if epi_ms > 0 else None
     return {"workload": "prefill_gated (same inputs) + per-head GroupNorm + swish gate",
             "ms_per_call": gated, "plain_ms_per_call": plain, "tokens_per_s": B * N / (gated * 1e-3),
+            "timing": "median of %d calls each" % steps,
             "epilogue": {"ms": epi_ms, "algorithmic_bytes": epi_bytes,
                          "roofline": {"kernel": "output_gate_kernel (in-place pass)", "bound": "hbm",
                                       "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": None if achieved is None else achieved / HBM_PEAK_GBS,
                                       "traffic": recorded_traffic("epilogue")}}}
+
+
+STREAM_LIB = os.path.join(ROOT, "yoco_gated_retention_amd", "libgret_stream.so")
+
+
+def bench_stream_ceiling(dp, reps=5):
+    """Measured HBM ceiling for the prefill's access mix: three read streams and
+    one write stream of one workload-sized array each (the prefill's own q, k,
+    v and output buffers), 16 bytes per lane, swept over the cache policy of
+    loads and stores, rows per lane (unroll) and workgroups per CU; plus the
+    read-only, write-only and copy rates of the same kernels. Median of `reps`
+    runs per variant; the best variant of each mix is reported."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(STREAM_LIB)
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.gret_stream_run.argtypes = [ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, i64, vp]
+    lib.gret_stream_run.restype = ci
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nbytes = dp.q.numel() * dp.q.element_size()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    a, b, c, o = ptr(dp.q), ptr(dp.k), ptr(dp.v), ptr(dp.out)
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run(reads, write, nl, ns, u, w):
+        def f():
+            rc = lib.gret_stream_run(reads, write, nl, ns, u, w * cus, a, b, c, o, nbytes, sp)
+            if rc != 0:
+                raise RuntimeError("gret_stream_run failed: %d" % rc)
+        return time_calls(f, reps, 2)[1]
+
+    def sweep(reads, write, pols, unrolls=(1, 2, 4, 8), per_cu=(1, 2, 4, 8)):
+        """Best variant overall and the best rate of each cache-policy pair."""
+        moved = nbytes * (reads + (1 if write else 0))
+        top, by_pol = None, {}
+        for (nl, ns) in pols:
+            for u in unrolls:
+                for w in per_cu:
+                    ms = run(reads, write, nl, ns, u, w)
+                    gbs = moved / (ms * 1e-3) / 1e9
+                    key = "%s_loads+%s_stores" % ("nt" if nl else "default", "nt" if ns else "wb")
+                    by_pol[key] = max(by_pol.get(key, 0.0), gbs)
+                    if top is None or gbs > top["GB/s"]:
+                        top = {"GB/s": gbs, "ms": ms, "nt_load": nl, "nt_store": ns, "unroll": u,
+                               "workgroups_per_cu": w}
+        return top, by_pol
+
+    res = {"array_bytes": nbytes, "timing": "median of %d runs per variant" % reps,
+           "kernel": "stream_kernel (libgret_stream.so): 16 B per lane, grid-stride, persistent"}
+    res["read3_write1"], res["read3_write1_by_policy"] = sweep(3, 1, [(1, 0), (0, 1), (0, 0),
+                                                                      (1, 1)])
+    res["read3"] = sweep(3, 0, [(1, 0), (0, 0)])[0]
+    res["copy"] = sweep(1, 1, [(1, 0), (0, 1), (0, 0), (1, 1)])[0]
+    res["write"] = sweep(0, 1, [(0, 0), (0, 1)], unrolls=(4,))[0]
+    return res
+
+
+def bench_gemm_peak(dev, n=8192, reps=10):
+    """Measured matrix-core rate: torch's library bf16 GEMM of n x n x n."""
+    import torch
+
+    g = torch.Generator(device=dev).manual_seed(1)
+    a = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    ms = time_calls(lambda: torch.matmul(a, b, out=c), reps, 3)[1]
+    del a, b, c
+    torch.cuda.empty_cache()
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"TFLOP/s": tf, "ms": ms, "shape": "%dx%dx%d bf16 (torch.matmul)" % (n, n, n),
+            "frac_of_spec": tf / BF16_PEAK_TFLOPS}
 
 
 def bench_decode_gated(gret, dev, d, reps=1, seed=4004):
@@ -609,30 +732,37 @@ def bench_decode(gret, dev, steps_total, reps, warmup_reps):
     return res, d
 
 
-def cpu_prefill_baseline(d, budget_s):
-    """The oracle's fp64 recurrence over all heads of the prefill workload, on
-    consecutive 64K-position pieces (state carried between them) until about
-    budget_s seconds have passed. The oracle computes every output row; only
-    keeping them (an fp64 copy of the whole output) is left out."""
+def cpu_prefill_baseline(d, budget_s, threads=None, piece=65536, label=None):
+    """The oracle's fp64 recurrence over all heads of a prefill workload, on
+    consecutive pieces of `piece` positions (state carried between them), until
+    about budget_s seconds have passed; a workload finished early is started
+    again. The oracle computes every output row; only keeping them (an fp64 copy
+    of the whole output) is left out."""
     import oracle
 
-    threads = cpu_threads()
+    threads = cpu_threads() if threads is None else threads
     B, H, N = d["q"].shape[:3]
-    piece = 65536
-    state = None
-    done, dt = 0, 0.0
-    while done < N and dt < budget_s:
-        sl = {x: np.ascontiguousarray(d[x][:, :, done:done + piece])
+    s0 = d.get("s0")
+    state = s0
+    pos, done, dt = 0, 0, 0.0
+    while dt < budget_s:
+        sl = {x: np.ascontiguousarray(d[x][:, :, pos:pos + piece])
               for x in ("q", "k", "v", "log_gamma")}
         t0 = time.time()
         _, state, _ = oracle.oracle_prefill_f64(sl["q"], sl["k"], sl["v"], sl["log_gamma"],
                                                 state_in=state, want_out=False, nthreads=threads)
         dt += time.time() - t0
-        done += sl["q"].shape[2]
+        n = sl["q"].shape[2]
+        done += n
+        pos += n
+        if pos >= N:
+            pos, state = 0, s0
     return {"value": B * done / dt, "unit": "tokens/s", "cores": min(threads, B * H),
             "kind": "oracle",
-            "sample": "positions 0..%d of all %d heads of the %d-position prefill (fp64 "
-                      "recurrence; every output computed, not kept, %.1f s)" % (done, B * H, N, dt)}
+            "sample": "%s: %d positions of all %d heads (fp64 recurrence in pieces of %d; every "
+                      "output computed, not kept, %.1f s on %d thread%s)" % (
+                          label or "prefill", done, B * H, piece, dt, threads,
+                          "" if threads == 1 else "s")}
 
 
 def cpu_decode_baseline(d, budget_s):
@@ -656,6 +786,176 @@ def cpu_decode_baseline(d, budget_s):
                 n, steps, B, H, dt)}
 
 
+def bench_prefill_legs(gret, dev, args):
+    """Every prefill leg: the headline workload (512K positions x 24 heads) with
+    its roofline against the spec and the measured stream ceiling, the same
+    workload with gates near 1, the chunk sweeps, the 1M workload with an
+    initial state, the fp32 tiny workload, the gated (epilogue) prefill, the
+    measured peaks and the CPU-oracle baselines."""
+    import torch
+
+    from workloads import CONFIGS, make_prefill_inputs, slow_decay_log_gamma
+
+    res = {}
+    chunk = args.chunk
+    kern = "gret_prefill (main + combine + prefix launches)"
+    cfg = CONFIGS["prefill_512k"]
+    t0 = time.time()
+    d3 = make_prefill_inputs("prefill_512k")
+    log("prefill inputs generated in %.1f s" % (time.time() - t0))
+    B, H, N, dk, dv = 1, cfg["H"], cfg["N"], cfg["dk"], cfg["dv"]
+    dp = DevicePrefill(gret, d3, dev)
+    ms, med, per = dp.time(chunk, args.steps, args.warmup)
+    peaks = {}
+    if not args.skip_peaks:
+        peaks["hbm_stream"] = bench_stream_ceiling(dp)
+        log("stream ceiling 3 reads + 1 write: %.0f GB/s (%s)" % (
+            peaks["hbm_stream"]["read3_write1"]["GB/s"],
+            json.dumps(peaks["hbm_stream"]["read3_write1_by_policy"])))
+        peaks["bf16_gemm"] = bench_gemm_peak(dev)
+        log("bf16 GEMM: %.0f TFLOP/s" % peaks["bf16_gemm"]["TFLOP/s"])
+    meas = peaks["hbm_stream"]["read3_write1"]["GB/s"] if peaks else None
+    roof = prefill_roofline(B, H, N, dk, dv, chunk, False, ms, kern, meas)
+    roof["traffic"] = recorded_traffic("prefill")
+    roof["mfma_busy_pct"] = recorded_mfma("prefill", "prefill_main_c64_kernel")
+    if peaks:
+        roof["mfma_peak_measured"] = peaks["bf16_gemm"]["TFLOP/s"]
+        roof["mfma_frac_measured"] = roof["mfma_tflops"] / peaks["bf16_gemm"]["TFLOP/s"]
+    res.update({
+        "value": B * N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+        "ms_median": med, "ms_min": min(per), "ms_max": max(per),
+        "config": {"workload": cfg["name"], "B": B, "H": H, "N": N, "dk": dk, "dv": dv,
+                   "chunk": chunk, "log_gamma": "fp32", "state": "fp32", "inputs": "bf16"},
+        "roofline": roof, "measured_peaks": peaks or None})
+    log("prefill chunk=%d: %.3f ms/step (median %.3f), %.3e tokens/s, %.0f GB/s (%.1f%% of HBM "
+        "peak%s)" % (chunk, ms, med, res["value"], roof["achieved"], 100 * roof["frac"],
+                     "" if not meas else ", %.1f%% of the measured stream ceiling" %
+                     (100 * roof["frac_measured"])))
+
+    # gates near 1 (u ~ N(4, 1)), same q, k, v
+    n_rep = max(10, args.steps // 2)
+    dp.set_log_gamma(slow_decay_log_gamma(B, H, N), dev)
+    _, med_slow, _ = dp.time(chunk, n_rep, 2)
+    res["prefill_slow_decay"] = {
+        "workload": cfg["name"] + "_gate_logit_n4_1",
+        "log_gamma": "u ~ N(4, 1), mean log-gate -0.0018 (gamma ~ 0.998), no sharp positions",
+        "ms_median": med_slow, "tokens_per_s": B * N / (med_slow * 1e-3),
+        "ratio_to_standard_median": med_slow / med,
+        "roofline": prefill_roofline(B, H, N, dk, dv, chunk, False, med_slow, kern, meas),
+        "timing": "median of %d calls" % n_rep}
+    log("prefill, gates near 1: %.3f ms (%.2fx the standard regime)" % (med_slow, med_slow / med))
+    dp.set_log_gamma(d3["log_gamma"], dev)
+
+    # chunk sizes at 512K
+    sweep = []
+    for ch in (64, 128, 256):
+        _, m, _ = dp.time(ch, n_rep, 2)
+        sweep.append({"chunk": ch, "ms_median": m, "tokens_per_s": B * N / (m * 1e-3),
+                      "roofline": prefill_roofline(B, H, N, dk, dv, ch, False, m, kern, meas)})
+        if ch != chunk:
+            dp.ws.pop(ch, None)  # keep one workspace resident at a time
+    res["prefill_512k_chunk_sweep"] = sweep
+    log("512K chunk sweep (ms): %s" % ", ".join("%d: %.3f" % (x["chunk"], x["ms_median"])
+                                                 for x in sweep))
+    if not args.skip_gated:
+        gp = time_prefill_gated(dp, chunk, n_rep, 2, dev)
+        res["prefill_gated"] = gp
+        log("prefill gated: %.3f ms/call (plain %.3f; epilogue %.3f ms)" % (
+            gp["ms_per_call"], gp["plain_ms_per_call"], gp["epilogue"]["ms"]))
+    dp.free()
+    del dp
+    if not args.skip_cpu:
+        res["cpu_baseline"] = cpu_prefill_baseline(d3, args.cpu_seconds, label=cfg["name"])
+        log("cpu baseline: %s" % json.dumps(res["cpu_baseline"]))
+    del d3
+
+    # configuration 2: 32K positions, chunk sizes 64 / 128 / 256
+    c2 = CONFIGS["prefill_32k"]
+    d2 = make_prefill_inputs("prefill_32k")
+    dp2 = DevicePrefill(gret, d2, dev)
+    sw2 = []
+    for ch in (64, 128, 256):
+        _, m, _ = dp2.time(ch, 20, 3)
+        sw2.append({"chunk": ch, "ms_median": m, "tokens_per_s": c2["N"] / (m * 1e-3),
+                    "roofline": prefill_roofline(1, c2["H"], c2["N"], c2["dk"], c2["dv"], ch,
+                                                 False, m, kern, meas)})
+    dp2.free()
+    res["prefill_32k_chunk_sweep"] = {"workload": c2["name"], "timing": "median of 20 calls",
+                                      "chunks": sw2}
+    log("32K chunk sweep (ms): %s" % ", ".join("%d: %.4f" % (x["chunk"], x["ms_median"])
+                                                for x in sw2))
+    if not args.skip_cpu:
+        res["prefill_32k_chunk_sweep"]["cpu_baseline_1thread"] = cpu_prefill_baseline(
+            d2, args.cpu_seconds, threads=1, piece=2048, label=c2["name"])
+    del d2
+
+    # configuration 4: 1M positions, nonzero initial state
+    c4 = CONFIGS["prefill_1m"]
+    t0 = time.time()
+    d4 = make_prefill_inputs("prefill_1m")
+    log("1M inputs generated in %.1f s" % (time.time() - t0))
+    dp4 = DevicePrefill(gret, d4, dev)
+    _, m4, per4 = dp4.time(chunk, 10, 2)
+    dp4.free()
+    del dp4, d4
+    res["prefill_1m"] = {"workload": c4["name"], "chunk": chunk, "ms_median": m4,
+                         "ms_min": min(per4), "tokens_per_s": c4["N"] / (m4 * 1e-3),
+                         "timing": "median of 10 calls",
+                         "roofline": prefill_roofline(1, c4["H"], c4["N"], c4["dk"], c4["dv"],
+                                                      chunk, True, m4, kern, meas)}
+    log("1M prefill: %.3f ms (%.1f%% of HBM peak)" % (
+        m4, 100 * res["prefill_1m"]["roofline"]["frac"]))
+
+    # configuration 1: fp32, 2 heads x 512, then 16 decode steps
+    res["tiny_f32"] = bench_tiny_f32(gret, dev, args)
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_tiny_f32(gret, dev, args):
+    """The fp32 tier: prefill of 2 heads x 512 (chunk 64) and the 16 decode steps
+    that follow, on the GPU; the oracle on one host thread beside it."""
+    import torch
+
+    import oracle
+    from workloads import CONFIGS, make_prefill_inputs
+
+    c1 = CONFIGS["tiny_f32"]
+    d = make_prefill_inputs("tiny_f32")
+    dp = DevicePrefill(gret, d, dev)
+    _, m, _ = dp.time(64, 20, 3)
+    steps = c1["decode_steps"]
+    toks = [[to_dev(d[x][t], dev) for x in ("dec_q", "dec_k", "dec_v", "dec_log_gamma")]
+            for t in range(steps)]
+    state = dp.so.clone()
+    out = torch.empty((1, c1["H"], c1["dv"]), dtype=torch.float32, device=dev)
+
+    def decode_all():
+        for t in range(steps):
+            gret.gret_decode_step(*toks[t], state, out=out)
+
+    _, md, _ = time_calls(decode_all, 10, 2)
+    dp.free()
+    res = {"workload": c1["name"], "prefill_ms_median": m, "tokens_per_s": c1["N"] / (m * 1e-3),
+           "decode_us_per_step": 1000.0 * md / steps, "timing": "median of 20 prefills; median "
+           "of 10 runs of the 16 decode steps"}
+    if not args.skip_cpu:
+        t0, n = time.time(), 0
+        while time.time() - t0 < 2.0:
+            _, s, _ = oracle.oracle_prefill_f64(d["q"], d["k"], d["v"], d["log_gamma"],
+                                                want_out=False, nthreads=1)
+            for t in range(steps):
+                oracle.oracle_decode_f64(d["dec_q"][t], d["dec_k"][t], d["dec_v"][t],
+                                         d["dec_log_gamma"][t], s, nthreads=1)
+            n += 1
+        dt = time.time() - t0
+        res["cpu_baseline_1thread"] = {
+            "value": n * c1["N"] / dt, "unit": "tokens/s (prefill + 16 decode steps)",
+            "cores": 1, "kind": "oracle",
+            "sample": "the whole workload %d times in %.1f s" % (n, dt)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -665,8 +965,8 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "xattn", "proj", "swa"], default=None)
     ap.add_argument("--decode-reps", type=int, default=1)
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time chunk 64/128/256 on the 32K and 512K workloads (stderr)")
+    ap.add_argument("--skip-peaks", action="store_true",
+                    help="skip the measured HBM stream ceiling and the library GEMM rate")
     ap.add_argument("--no-swa-decode", action="store_true",
                     help="skip the sliding-window decode timing (it runs on the cross-attention "
                          "kernels, whose counter runs should see only the cross-attention calls)")
@@ -718,53 +1018,9 @@ def main():
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
               "data": "synthetic (seeded; value distributions of the pages' gRet gate)"}
 
-    d3 = None
+    result["host_cpu"] = cpu_info()
     if args.only in (None, "prefill"):
-        cfg = CONFIGS["prefill_512k"]
-        t0 = time.time()
-        d3 = make_prefill_inputs("prefill_512k")
-        log("prefill inputs generated in %.1f s" % (time.time() - t0))
-        ms = time_prefill(gret, d3, args.chunk, args.steps, args.warmup, dev)
-        B, H, N, dk, dv = 1, cfg["H"], cfg["N"], cfg["dk"], cfg["dv"]
-        nbytes, flops = prefill_algorithmic(B, H, N, dk, dv, args.chunk, False)
-        achieved = nbytes / (ms * 1e-3) / 1e9
-        result.update({
-            "value": B * N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
-            "config": {"workload": cfg["name"], "B": B, "H": H, "N": N, "dk": dk, "dv": dv,
-                       "chunk": args.chunk, "log_gamma": "fp32", "state": "fp32",
-                       "inputs": "bf16"},
-            "roofline": {"kernel": "gret_prefill (main + combine + prefix launches)",
-                         "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                         "traffic": recorded_traffic("prefill"),
-                         "algorithmic_bytes_per_launch": nbytes,
-                         "mfma_tflops": flops / (ms * 1e-3) / 1e12,
-                         "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                         "mfma_busy_pct": recorded_mfma("prefill", "prefill_main_c64_kernel")},
-        })
-        log("prefill chunk=%d: %.3f ms/step, %.3e tokens/s, %.0f GB/s (%.1f%% of HBM peak)" % (
-            args.chunk, ms, result["value"], achieved, 100 * achieved / HBM_PEAK_GBS))
-        if args.sweep:
-            for cid in ("prefill_32k", "prefill_512k"):
-                dd = d3 if cid == "prefill_512k" else make_prefill_inputs(cid)
-                c = CONFIGS[cid]
-                for ch in (64, 128, 256):
-                    m = time_prefill(gret, dd, ch, max(3, args.steps // 2), 2, dev)
-                    nb, fl = prefill_algorithmic(1, c["H"], c["N"], c["dk"], c["dv"], ch, False)
-                    log(json.dumps({"sweep": c["name"], "chunk": ch, "ms": m,
-                                    "tokens_per_s": c["N"] / (m * 1e-3),
-                                    "hbm_frac": nb / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                    "mfma_frac": fl / (m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}))
-        if not args.skip_gated:
-            gp = time_prefill_gated(gret, d3, args.chunk, max(5, args.steps // 2), 2, dev)
-            result["prefill_gated"] = gp
-            log("prefill gated: %.3f ms/call (plain %.3f; epilogue pass %.3f ms, %s GB/s)" % (
-                gp["ms_per_call"], gp["plain_ms_per_call"], gp["epilogue"]["ms"],
-                "%.0f" % gp["epilogue"]["roofline"]["achieved"]
-                if gp["epilogue"]["roofline"]["achieved"] else "n/a"))
-        if not args.skip_cpu:
-            result["cpu_baseline"] = cpu_prefill_baseline(d3, args.cpu_seconds)
-            log("cpu baseline: %s" % json.dumps(result["cpu_baseline"]))
+        result.update(bench_prefill_legs(gret, dev, args))
 
     if args.only in (None, "xattn"):
         xa = [bench_cross_attention(gret, dev, 1, 524288,

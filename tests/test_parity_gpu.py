@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from tests.gpu_util import as_f64, eps, stats_eps, to_dev, to_host
-from workloads import CONFIGS, make_decode_inputs, make_prefill_inputs
+from workloads import CONFIGS, make_decode_inputs, make_prefill_inputs, slow_decay_log_gamma
 
 pytestmark = pytest.mark.gpu
 
@@ -249,43 +249,54 @@ def test_prefill_32k_full(gret, chunk):
     assert e_o <= TOL_BF16 and e_s <= TOL_BF16
 
 
-SAMPLE_HEADS = (0, 11, 23)
-
-
-def _sampled_check(gret, workload, chunk, first_chunk=False):
+def _full_check(gret, workload, chunk, first_chunk=False, log_gamma=None):
+    """Every head of a full-size workload against the oracle, which compares
+    each output element as it goes (nothing of the size of the output is kept
+    in float64). Per-head eps is reported; the bar is the global eps."""
     d = make_prefill_inputs(workload)
+    if log_gamma is not None:
+        d["log_gamma"] = log_gamma
     s0 = d["s0"]
-    say("%s N=%d chunk=%d (oracle on heads %s)" % (workload, d["N"], chunk, SAMPLE_HEADS))
+    say("%s N=%d chunk=%d, oracle on all %d heads" % (workload, d["N"], chunk, d["H"]))
     out, st = gpu_prefill(gret, d, chunk, s0)
-    hs = list(SAMPLE_HEADS)
-
-    def sl(a):
-        return np.ascontiguousarray(a[:, hs])
-
-    _, s_ref, stats = oracle.oracle_prefill_f64(sl(d["q"]), sl(d["k"]), sl(d["v"]),
-                                                sl(d["log_gamma"]),
-                                                None if s0 is None else sl(s0),
-                                                want_out=False, compare=sl(out))
-    e_o, e_s = stats_eps(stats), eps(st[:, hs], s_ref)
-    say("   eps_out=%.3e eps_state=%.3e" % (e_o, e_s))
+    _, s_ref, stats = oracle.oracle_prefill_f64(d["q"], d["k"], d["v"], d["log_gamma"], s0,
+                                                want_out=False, compare=out)
+    e_o, e_s = stats_eps(stats), eps(st, s_ref)
+    per_head = stats[:, 0] / stats[:, 1]
+    say("   eps_out=%.3e eps_state=%.3e per-head eps max %.3e (head %d) min %.3e" % (
+        e_o, e_s, per_head.max(), int(per_head.argmax()), per_head.min()))
     assert e_o <= TOL_BF16 and e_s <= TOL_BF16
     if first_chunk:
-        # the initial state decays within a few hundred positions; check it alone
+        # the initial state decays within a few hundred positions; its effect
+        # is checked on its own over the first chunk of every head
         n = chunk
-        o_ref, _, _ = oracle.oracle_prefill_f64(sl(d["q"][:, :, :n]), sl(d["k"][:, :, :n]),
-                                                sl(d["v"][:, :, :n]), sl(d["log_gamma"][:, :, :n]),
-                                                sl(s0))
-        e_f = eps(out[:, hs, :n], o_ref)
+        o_ref, _, _ = oracle.oracle_prefill_f64(
+            np.ascontiguousarray(d["q"][:, :, :n]), np.ascontiguousarray(d["k"][:, :, :n]),
+            np.ascontiguousarray(d["v"][:, :, :n]),
+            np.ascontiguousarray(d["log_gamma"][:, :, :n]), s0)
+        e_f = eps(out[:, :, :n], o_ref)
         say("   first-chunk eps=%.3e" % e_f)
         assert e_f <= TOL_BF16
 
 
-def test_prefill_512k_sampled_heads(gret):
-    _sampled_check(gret, "prefill_512k", 64)
+@pytest.mark.timeout(900)
+def test_prefill_512k_all_heads(gret):
+    _full_check(gret, "prefill_512k", 64)
 
 
-def test_prefill_1m_sampled_heads(gret):
-    _sampled_check(gret, "prefill_1m", 64, first_chunk=True)
+@pytest.mark.timeout(900)
+def test_prefill_1m_all_heads(gret):
+    _full_check(gret, "prefill_1m", 64, first_chunk=True)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_512k_slow_decay_all_heads(gret):
+    """The 512K workload with gates near 1 (u ~ N(4, 1): mean log-gate about
+    -0.0018), where a segment's incoming state stays alive over most of the
+    segment and the schedule recomputes the most."""
+    cfg = CONFIGS["prefill_512k"]
+    lg = slow_decay_log_gamma(cfg["B"], cfg["H"], cfg["N"])
+    _full_check(gret, "prefill_512k", 64, log_gamma=lg)
 
 
 # ------------------------------------------------------------------ decode
@@ -314,35 +325,29 @@ def test_decode_small(gret, dtype, dk, dv):
     assert eps(to_host(o), o_r) <= tol and eps(to_host(so), z) <= tol
 
 
-def test_decode_b256_1000_steps_sampled(gret):
+@pytest.mark.timeout(900)
+def test_decode_b256_1000_steps_all_heads(gret):
     cfg = CONFIGS["decode_b256"]
     B, H, steps = cfg["B"], cfg["H"], cfg["decode_steps"]
-    rng = np.random.default_rng(5)
-    heads = sorted(rng.choice(B * H, 48, replace=False).tolist())
-    say("decode_b256 B=%d H=%d steps=%d, oracle on %d heads" % (B, H, steps, len(heads)))
-    d = make_decode_inputs("decode_b256", heads=heads)
+    say("decode_b256 B=%d H=%d steps=%d, oracle on all heads and steps" % (B, H, steps))
+    d = make_decode_inputs("decode_b256")
     state = to_dev(d["state"])
     q, k, v, lg = (to_dev(d[key]) for key in ("q", "k", "v", "log_gamma"))
-    hidx = torch.tensor(heads, device="cuda")
-    outs = []
+    outs = torch.empty((steps, B, H, 128), dtype=torch.bfloat16, device="cuda")
     for t in range(steps):
-        o = gret.gret_decode_step(q[t], k[t], v[t], lg[t], state)
-        outs.append(o.view(B * H, -1).index_select(0, hidx))
+        gret.gret_decode_step(q[t], k[t], v[t], lg[t], state, out=outs[t])
     torch.cuda.synchronize()
-    outs = to_host(torch.stack(outs))
-    st = to_host(state).reshape(B * H, 128, 128)[heads]
-    flat = lambda a: a.reshape((a.shape[0], B * H) + a.shape[3:])[:, heads]  # noqa: E731
-    s64 = d["state"].reshape(B * H, 128, 128)[heads].astype(np.float64)
-    qh, kh, vh = flat(d["q"]), flat(d["k"]), flat(d["v"])
-    lh = d["log_gamma"].reshape(steps, B * H)[:, heads]
-    worst = 0.0
+    outs = to_host(outs)
+    st = to_host(state)
+    s64 = d["state"].astype(np.float64)
+    worst, worst_t = 0.0, -1
     for t in range(steps):
-        o_r = oracle.oracle_decode_f64(np.ascontiguousarray(qh[t]), np.ascontiguousarray(kh[t]),
-                                       np.ascontiguousarray(vh[t]), np.ascontiguousarray(lh[t]),
-                                       s64)
-        worst = max(worst, eps(outs[t], o_r))
+        o_r = oracle.oracle_decode_f64(d["q"][t], d["k"][t], d["v"][t], d["log_gamma"][t], s64)
+        e = eps(outs[t], o_r)
+        if e > worst:
+            worst, worst_t = e, t
     e_s = eps(st, s64)
-    say("   worst per-step eps=%.3e final-state eps=%.3e" % (worst, e_s))
+    say("   worst per-step eps=%.3e (step %d) final-state eps=%.3e" % (worst, worst_t, e_s))
     assert worst <= TOL_BF16 and e_s <= TOL_BF16
 
 

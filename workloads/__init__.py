@@ -14,4 +14,5 @@ from .gret_inputs import (  # noqa: F401
     make_prefill_inputs,
     make_projection_inputs,
     prefill_head,
+    slow_decay_log_gamma,
 )

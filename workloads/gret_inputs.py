@@ -165,6 +165,30 @@ def make_prefill_inputs(workload: str, *, N: int | None = None, B: int | None = 
                 dec_v=dvv, B=B, H=H, N=N, dk=dk, dv=dv, dtype=dtype)
 
 
+# Gates near 1: the temperature on the page keeps gamma close to 1 so that the
+# state forgets slowly (section "路线二：Multi-Head Gated Retention"). This
+# regime draws the gate logit from N(4, 1): gamma = sigmoid(u)^(1/16) has mean
+# about 0.998 and the mean log-gate is about -0.0018.
+SLOW_DECAY_SEED = 1013
+SLOW_DECAY_LOGIT_MEAN = 4.0
+
+
+def slow_decay_log_gamma(B: int, H: int, N: int, seed: int = SLOW_DECAY_SEED) -> np.ndarray:
+    """log_gamma [B,H,N] float32 with u ~ N(4, 1) per (head, position), one PCG64
+    stream per flattened head (child i of SeedSequence(seed)); same mapping
+    from u to the log-gate as every other workload."""
+    lg = np.empty((B, H, N), np.float32)
+
+    def one(x):
+        b, h = divmod(x, H)
+        u = _rng(seed, x).standard_normal(N, dtype=np.float32) + np.float32(SLOW_DECAY_LOGIT_MEAN)
+        lg[b, h] = _log_gamma(u)
+
+    with ThreadPoolExecutor(_workers(B * H)) as ex:
+        list(ex.map(one, range(B * H)))
+    return lg
+
+
 def make_decode_inputs(workload: str = "decode_b256", *, B: int | None = None, H: int | None = None,
                        steps: int | None = None, heads=None):
     """Batched decode workload: initial state [B,H,dk,dv] (std cfg s0_std) and a

@@ -119,23 +119,62 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
 
 
-def _check_dev(name, t, dtype=None):
+def _check_dev(name, t, dtype=None, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
     if t.device.type != "cuda":
         raise ValueError("%s must be a GPU tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s (q's device), got %s" % (name, device, t.device))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     if dtype is not None and t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
 
 
+def _check_tensors(specs, device):
+    """specs: (name, tensor or None, exact shape or None, dtype or None). Every
+    shape is checked before anything else, so a wrong-sized buffer is rejected
+    before any device or library call; then dtype, device (q's GPU) and
+    contiguity. The kernels take every size from q and v, so an undersized
+    output, state or ring buffer would otherwise be written out of bounds."""
+    for name, t, shape, _ in specs:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape),
+                                                               tuple(t.shape)))
+    for name, t, _, dtype in specs:
+        if t is not None:
+            _check_dev(name, t, dtype, device)
+
+
+def _check_workspace(workspace, device):
+    if workspace is not None:
+        _check_dev("workspace", workspace, None, device)
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _call(device, fn, *args):
+    """Calls a library entry point with q's device current (the library asks
+    the runtime for the current device's compute-unit count)."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return fn(*args)
+    with torch.cuda.device(device):
+        return fn(*args)
+
+
+def _bytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, dtype) -> int:
@@ -148,45 +187,41 @@ def gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, dtype) -> int:
     return int(n.value)
 
 
-def _prefill_setup(q, k, v, log_gamma, state_in, chunk, out, state_out, workspace):
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, q.dtype)
-    _check_dev("log_gamma", log_gamma, torch.float32)
-    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+def _prefill_shapes(q, v):
+    for name, t in (("q", q), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+    if q.dim() != 4 or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B,H,N,dk] and v [B,H,N,dv]")
     B, H, N, dk = q.shape
-    dv = v.shape[3]
-    if tuple(log_gamma.shape) != (B, H, N):
-        raise ValueError("log_gamma must be [B,H,N]")
-    if state_in is not None:
-        _check_dev("state_in", state_in, torch.float32)
-        if tuple(state_in.shape) != (B, H, dk, dv):
-            raise ValueError("state_in must be [B,H,dk,dv]")
-    if out is None:
-        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
-    else:
-        _check_dev("out", out, q.dtype)
-    if state_out is None:
-        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
-    else:
-        _check_dev("state_out", state_out, torch.float32)
+    return B, H, N, dk, v.shape[3]
+
+
+def _prefill_setup(q, k, v, log_gamma, state_in, chunk, out, state_out, workspace, extra=()):
+    B, H, N, dk, dv = _prefill_shapes(q, v)
+    dev = q.device
+    _check_tensors([("q", q, None, None), ("k", k, q.shape, q.dtype), ("v", v, None, q.dtype),
+                    ("log_gamma", log_gamma, (B, H, N), torch.float32),
+                    ("state_in", state_in, (B, H, dk, dv), torch.float32),
+                    ("out", out, (B, H, N, dv), q.dtype),
+                    ("state_out", state_out, (B, H, dk, dv), torch.float32)] + list(extra), dev)
+    _check_workspace(workspace, dev)
     code = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=dev)
+    if state_out is None:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     need = gret_prefill_workspace_bytes(B, H, N, dk, dv, chunk, code)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    return (B, H, N, dk, dv, code, out, state_out, workspace, ws_bytes)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    return (B, H, N, dk, dv, code, out, state_out, workspace, _bytes(workspace))
 
 
-def _check_epilogue(gate, like, norm_weight, norm_bias, H, dv):
-    _check_dev("gate", gate, like.dtype)
-    if tuple(gate.shape) != tuple(like.shape):
-        raise ValueError("gate must have the output's shape %s" % (tuple(like.shape),))
-    for name, t in (("norm_weight", norm_weight), ("norm_bias", norm_bias)):
-        if t is not None:
-            _check_dev(name, t, torch.float32)
-            if tuple(t.shape) != (H, dv):
-                raise ValueError("%s must be [H, dv]" % name)
+def _epilogue_specs(gate, shape, dtype, norm_weight, norm_bias, H, dv):
+    if gate is None:
+        raise ValueError("gate is required")
+    return [("gate", gate, shape, dtype), ("norm_weight", norm_weight, (H, dv), torch.float32),
+            ("norm_bias", norm_bias, (H, dv), torch.float32)]
 
 
 def gret_prefill(q, k, v, log_gamma, state_in=None, chunk=64, out=None, state_out=None,
@@ -196,9 +231,9 @@ def gret_prefill(q, k, v, log_gamma, state_in=None, chunk=64, out=None, state_ou
     lib = load_library()
     B, H, N, dk, dv, code, out, state_out, workspace, ws_bytes = _prefill_setup(
         q, k, v, log_gamma, state_in, chunk, out, state_out, workspace)
-    st = lib.gret_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(state_in), _ptr(out),
-                          _ptr(state_out), B, H, N, dk, dv, chunk, code, _ptr(workspace), ws_bytes,
-                          _stream())
+    st = _call(q.device, lib.gret_prefill, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma),
+               _ptr(state_in), _ptr(out), _ptr(state_out), B, H, N, dk, dv, chunk, code,
+               _ptr(workspace), ws_bytes, _stream(q.device))
     if st != GRET_OK:
         raise GretError(st, "gret_prefill")
     return out, state_out
@@ -210,41 +245,44 @@ def gret_prefill_gated(q, k, v, log_gamma, gate, state_in=None, norm_weight=None
     GroupNorm_per_head(retention output). gate [B,H,N,dv] in q's dtype;
     norm_weight, norm_bias [H,dv] fp32 or None. Returns (out, state_out)."""
     lib = load_library()
+    B, H, N, dk, dv = _prefill_shapes(q, v)
+    extra = _epilogue_specs(gate, (B, H, N, dv), q.dtype, norm_weight, norm_bias, H, dv)
     B, H, N, dk, dv, code, out, state_out, workspace, ws_bytes = _prefill_setup(
-        q, k, v, log_gamma, state_in, chunk, out, state_out, workspace)
-    _check_epilogue(gate, out, norm_weight, norm_bias, H, dv)
-    st = lib.gret_prefill_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(state_in),
-                                _ptr(gate), _ptr(norm_weight), _ptr(norm_bias), float(norm_eps),
-                                _ptr(out), _ptr(state_out), B, H, N, dk, dv, chunk, code,
-                                _ptr(workspace), ws_bytes, _stream())
+        q, k, v, log_gamma, state_in, chunk, out, state_out, workspace, extra)
+    st = _call(q.device, lib.gret_prefill_gated, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma),
+               _ptr(state_in), _ptr(gate), _ptr(norm_weight), _ptr(norm_bias), float(norm_eps),
+               _ptr(out), _ptr(state_out), B, H, N, dk, dv, chunk, code, _ptr(workspace),
+               ws_bytes, _stream(q.device))
     if st != GRET_OK:
         raise GretError(st, "gret_prefill_gated")
     return out, state_out
 
 
-def _decode_setup(q, k, v, log_gamma, state_in, out, state_out):
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, q.dtype)
-    _check_dev("log_gamma", log_gamma, torch.float32)
-    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+def _decode_shapes(q, v):
+    for name, t in (("q", q), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+    if q.dim() != 3 or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
         raise ValueError("q, k must be [B,H,dk] and v [B,H,dv]")
     B, H, dk = q.shape
-    dv = v.shape[2]
-    if tuple(log_gamma.shape) != (B, H):
-        raise ValueError("log_gamma must be [B,H]")
-    if state_in is not None:
-        _check_dev("state_in", state_in, torch.float32)
+    return B, H, dk, v.shape[2]
+
+
+def _decode_setup(q, k, v, log_gamma, state_in, out, state_out, extra=()):
+    B, H, dk, dv = _decode_shapes(q, v)
+    dev = q.device
     if state_out is None:
         if state_in is None:
             raise ValueError("state_out is required when state_in is None")
         state_out = state_in
-    _check_dev("state_out", state_out, torch.float32)
-    if tuple(state_out.shape) != (B, H, dk, dv):
-        raise ValueError("state must be [B,H,dk,dv]")
+    _check_tensors([("q", q, None, None), ("k", k, q.shape, q.dtype), ("v", v, None, q.dtype),
+                    ("log_gamma", log_gamma, (B, H), torch.float32),
+                    ("state_in", state_in, (B, H, dk, dv), torch.float32),
+                    ("state_out", state_out, (B, H, dk, dv), torch.float32),
+                    ("out", out, (B, H, dv), q.dtype)] + list(extra), dev)
+    _dtype_code(q)
     if out is None:
-        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
-    else:
-        _check_dev("out", out, q.dtype)
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
     return B, H, dk, dv, out, state_out
 
 
@@ -254,8 +292,9 @@ def gret_decode_step(q, k, v, log_gamma, state_in, out=None, state_out=None):
     (in-place update). Returns out [B,H,dv]."""
     lib = load_library()
     B, H, dk, dv, out, state_out = _decode_setup(q, k, v, log_gamma, state_in, out, state_out)
-    st = lib.gret_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(state_in),
-                              _ptr(out), _ptr(state_out), B, H, dk, dv, _dtype_code(q), _stream())
+    st = _call(q.device, lib.gret_decode_step, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma),
+               _ptr(state_in), _ptr(out), _ptr(state_out), B, H, dk, dv, _dtype_code(q),
+               _stream(q.device))
     if st != GRET_OK:
         raise GretError(st, "gret_decode_step")
     return out
@@ -266,12 +305,13 @@ def gret_decode_step_gated(q, k, v, log_gamma, state_in, gate, norm_weight=None,
     """One recurrent step with the output epilogue fused into its store:
     out = swish(gate) * GroupNorm_per_head(q S). gate [B,H,dv] in q's dtype."""
     lib = load_library()
-    B, H, dk, dv, out, state_out = _decode_setup(q, k, v, log_gamma, state_in, out, state_out)
-    _check_epilogue(gate, out, norm_weight, norm_bias, H, dv)
-    st = lib.gret_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(state_in),
-                                    _ptr(gate), _ptr(norm_weight), _ptr(norm_bias),
-                                    float(norm_eps), _ptr(out), _ptr(state_out), B, H, dk, dv,
-                                    _dtype_code(q), _stream())
+    B, H, dk, dv = _decode_shapes(q, v)
+    extra = _epilogue_specs(gate, (B, H, dv), q.dtype, norm_weight, norm_bias, H, dv)
+    B, H, dk, dv, out, state_out = _decode_setup(q, k, v, log_gamma, state_in, out, state_out,
+                                                 extra)
+    st = _call(q.device, lib.gret_decode_step_gated, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma),
+               _ptr(state_in), _ptr(gate), _ptr(norm_weight), _ptr(norm_bias), float(norm_eps),
+               _ptr(out), _ptr(state_out), B, H, dk, dv, _dtype_code(q), _stream(q.device))
     if st != GRET_OK:
         raise GretError(st, "gret_decode_step_gated")
     return out
@@ -292,32 +332,30 @@ def gret_cross_attention_decode(q, k_cache, v_cache, lengths=None, scale=None, o
     [B] on the GPU or None (all L); scale defaults to d^-1/2. Returns out
     [B,Hq,d] bf16."""
     lib = load_library()
-    _check_dev("q", q, torch.bfloat16)
-    _check_dev("k_cache", k_cache, torch.bfloat16)
-    _check_dev("v_cache", v_cache, torch.bfloat16)
-    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+    for name, t in (("q", q), ("k_cache", k_cache)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+    if q.dim() != 3 or k_cache.dim() != 4:
         raise ValueError("q must be [B,Hq,d] and the caches [B,Hkv,L,d]")
     B, Hq, d = q.shape
-    _, Hkv, L, dk = k_cache.shape
-    if k_cache.shape[0] != B or dk != d:
-        raise ValueError("cache shape does not match q")
-    if lengths is not None:
-        _check_dev("lengths", lengths, torch.int32)
-        if tuple(lengths.shape) != (B,):
-            raise ValueError("lengths must be [B]")
+    _, Hkv, L, _ = k_cache.shape
+    dev = q.device
+    _check_tensors([("q", q, None, torch.bfloat16),
+                    ("k_cache", k_cache, (B, Hkv, L, d), torch.bfloat16),
+                    ("v_cache", v_cache, (B, Hkv, L, d), torch.bfloat16),
+                    ("lengths", lengths, (B,), torch.int32),
+                    ("out", out, (B, Hq, d), torch.bfloat16)], dev)
+    _check_workspace(workspace, dev)
     if scale is None:
         scale = d ** -0.5
     if out is None:
-        out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
-    else:
-        _check_dev("out", out, torch.bfloat16)
-    need = gret_cross_attention_workspace_bytes(B, Hq, Hkv, L, d)
+        out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.gret_cross_attention_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lengths),
-                                         _ptr(out), B, Hq, Hkv, L, d, float(scale),
-                                         GRET_DTYPE_BF16, _ptr(workspace), ws_bytes, _stream())
+        need = gret_cross_attention_workspace_bytes(B, Hq, Hkv, L, d)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = _call(dev, lib.gret_cross_attention_decode, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+               _ptr(lengths), _ptr(out), B, Hq, Hkv, L, d, float(scale), GRET_DTYPE_BF16,
+               _ptr(workspace), _bytes(workspace), _stream(dev))
     if st != GRET_OK:
         raise GretError(st, "gret_cross_attention_decode")
     return out
@@ -330,39 +368,37 @@ def gret_head_projection(x, w_key, w_gamma=None, key_scale=1.0, temperature=16.0
     log(sigmoid(x w_gamma^T)) / temperature -> log_gamma [B,H,N] fp32 (else
     None). H is taken from w_gamma, or must be given without it."""
     lib = load_library()
-    _check_dev("x", x, torch.bfloat16)
-    _check_dev("w_key", w_key, torch.bfloat16)
+    for name, t in (("x", x), ("w_key", w_key)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
     if x.dim() != 3 or w_key.dim() != 2 or w_key.shape[1] != x.shape[2]:
         raise ValueError("x must be [B,N,D] and w_key [H*dk, D]")
     B, N, D = x.shape
     if w_gamma is not None:
-        _check_dev("w_gamma", w_gamma, torch.bfloat16)
+        if not isinstance(w_gamma, torch.Tensor):
+            raise TypeError("w_gamma must be a torch.Tensor")
         if w_gamma.dim() != 2 or w_gamma.shape[1] != D:
             raise ValueError("w_gamma must be [H, D]")
         if H is not None and H != w_gamma.shape[0]:
             raise ValueError("H does not match w_gamma")
         H = w_gamma.shape[0]
+    elif log_gamma is not None:
+        raise ValueError("log_gamma needs w_gamma")
     if H is None or H < 1 or w_key.shape[0] % H != 0:
         raise ValueError("w_key must have H * dk rows")
     dk = w_key.shape[0] // H
+    dev = x.device
+    _check_tensors([("x", x, None, torch.bfloat16), ("w_key", w_key, None, torch.bfloat16),
+                    ("w_gamma", w_gamma, None, torch.bfloat16),
+                    ("k_out", k_out, (B, H, N, dk), torch.bfloat16),
+                    ("log_gamma", log_gamma, (B, H, N), torch.float32)], dev)
     if k_out is None:
-        k_out = torch.empty((B, H, N, dk), dtype=torch.bfloat16, device=x.device)
-    else:
-        _check_dev("k_out", k_out, torch.bfloat16)
-        if tuple(k_out.shape) != (B, H, N, dk):
-            raise ValueError("k_out must be [B,H,N,dk]")
-    if w_gamma is not None:
-        if log_gamma is None:
-            log_gamma = torch.empty((B, H, N), dtype=torch.float32, device=x.device)
-        else:
-            _check_dev("log_gamma", log_gamma, torch.float32)
-            if tuple(log_gamma.shape) != (B, H, N):
-                raise ValueError("log_gamma must be [B,H,N]")
-    elif log_gamma is not None:
-        raise ValueError("log_gamma needs w_gamma")
-    st = lib.gret_head_projection(_ptr(x), _ptr(w_key), _ptr(w_gamma), float(key_scale),
-                                  float(temperature), _ptr(k_out), _ptr(log_gamma), B, N, D, H,
-                                  dk, GRET_DTYPE_BF16, _stream())
+        k_out = torch.empty((B, H, N, dk), dtype=torch.bfloat16, device=dev)
+    if w_gamma is not None and log_gamma is None:
+        log_gamma = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    st = _call(dev, lib.gret_head_projection, _ptr(x), _ptr(w_key), _ptr(w_gamma),
+               float(key_scale), float(temperature), _ptr(k_out), _ptr(log_gamma), B, N, D, H,
+               dk, GRET_DTYPE_BF16, _stream(dev))
     if st != GRET_OK:
         raise GretError(st, "gret_head_projection")
     return k_out, log_gamma
@@ -373,30 +409,29 @@ def gret_swa_prefill(q, k, v, window, scale=None, out=None, k_ring=None, v_ring=
     (bf16) with `window` positions per query; fills k_ring, v_ring
     [B,Hkv,window,d] with the last positions when given. Returns out."""
     lib = load_library()
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, torch.bfloat16)
-    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+    for name, t in (("q", q), ("k", k)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+    if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q must be [B,Hq,N,d] and k, v [B,Hkv,N,d]")
     B, Hq, N, d = q.shape
-    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
-        raise ValueError("k, v do not match q")
     Hkv = k.shape[1]
     if (k_ring is None) != (v_ring is None):
         raise ValueError("give both rings or neither")
-    if k_ring is not None:
-        for name, t in (("k_ring", k_ring), ("v_ring", v_ring)):
-            _check_dev(name, t, torch.bfloat16)
-            if tuple(t.shape) != (B, Hkv, window, d):
-                raise ValueError("%s must be [B,Hkv,window,d]" % name)
+    window = int(window)
+    dev = q.device
+    _check_tensors([("q", q, None, torch.bfloat16), ("k", k, (B, Hkv, N, d), torch.bfloat16),
+                    ("v", v, (B, Hkv, N, d), torch.bfloat16),
+                    ("out", out, (B, Hq, N, d), torch.bfloat16),
+                    ("k_ring", k_ring, (B, Hkv, window, d), torch.bfloat16),
+                    ("v_ring", v_ring, (B, Hkv, window, d), torch.bfloat16)], dev)
     if scale is None:
         scale = d ** -0.5
     if out is None:
         out = torch.empty_like(q)
-    else:
-        _check_dev("out", out, torch.bfloat16)
-    st = lib.gret_swa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(k_ring), _ptr(v_ring),
-                              B, Hq, Hkv, N, d, int(window), float(scale), GRET_DTYPE_BF16,
-                              _stream())
+    st = _call(dev, lib.gret_swa_prefill, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(k_ring),
+               _ptr(v_ring), B, Hq, Hkv, N, d, window, float(scale), GRET_DTYPE_BF16,
+               _stream(dev))
     if st != GRET_OK:
         raise GretError(st, "gret_swa_prefill")
     return out
@@ -417,30 +452,32 @@ def gret_swa_decode_step(q, k_new, v_new, k_ring, v_ring, positions, scale=None,
     place), then q [B,Hq,d] attends over the valid slots. positions: int32 [B]
     on the GPU. Returns out [B,Hq,d] bf16."""
     lib = load_library()
-    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_ring", k_ring),
-                    ("v_ring", v_ring)):
-        _check_dev(name, t, torch.bfloat16)
-    _check_dev("positions", positions, torch.int32)
-    if q.dim() != 3 or k_ring.dim() != 4 or v_ring.shape != k_ring.shape:
+    for name, t in (("q", q), ("k_ring", k_ring)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+    if q.dim() != 3 or k_ring.dim() != 4:
         raise ValueError("q must be [B,Hq,d] and the rings [B,Hkv,window,d]")
     B, Hq, d = q.shape
-    _, Hkv, window, dr = k_ring.shape
-    if k_ring.shape[0] != B or dr != d or tuple(k_new.shape) != (B, Hkv, d) or \
-            v_new.shape != k_new.shape or tuple(positions.shape) != (B,):
-        raise ValueError("shapes do not match")
+    _, Hkv, window, _ = k_ring.shape
+    dev = q.device
+    _check_tensors([("q", q, None, torch.bfloat16),
+                    ("k_new", k_new, (B, Hkv, d), torch.bfloat16),
+                    ("v_new", v_new, (B, Hkv, d), torch.bfloat16),
+                    ("k_ring", k_ring, (B, Hkv, window, d), torch.bfloat16),
+                    ("v_ring", v_ring, (B, Hkv, window, d), torch.bfloat16),
+                    ("positions", positions, (B,), torch.int32),
+                    ("out", out, (B, Hq, d), torch.bfloat16)], dev)
+    _check_workspace(workspace, dev)
     if scale is None:
         scale = d ** -0.5
     if out is None:
         out = torch.empty_like(q)
-    else:
-        _check_dev("out", out, torch.bfloat16)
-    need = gret_swa_decode_workspace_bytes(B, Hq, Hkv, window, d)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.gret_swa_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_ring), _ptr(v_ring),
-                                  _ptr(positions), _ptr(out), B, Hq, Hkv, window, d, float(scale),
-                                  GRET_DTYPE_BF16, _ptr(workspace), ws_bytes, _stream())
+        need = gret_swa_decode_workspace_bytes(B, Hq, Hkv, window, d)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = _call(dev, lib.gret_swa_decode_step, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_ring),
+               _ptr(v_ring), _ptr(positions), _ptr(out), B, Hq, Hkv, window, d, float(scale),
+               GRET_DTYPE_BF16, _ptr(workspace), _bytes(workspace), _stream(dev))
     if st != GRET_OK:
         raise GretError(st, "gret_swa_decode_step")
     return out
