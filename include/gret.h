@@ -22,7 +22,9 @@
  * ---------------------------------------
  * Pointers. Every tensor pointer is a device pointer owned by the caller. The
  *   library never allocates device memory, never frees or retains a pointer
- *   after the call returns, keeps no global state and is reentrant.
+ *   after the call returns, keeps no global state and is reentrant -- with one
+ *   exception, gret_prefill_noalloc, which uses a fixed device array of the
+ *   library's own in place of the caller's workspace (see there).
  * Layouts (contiguous, row-major, head-major as [batch, head, position, dim]):
  *   prefill  q, k [B,H,N,dk]; v, out [B,H,N,dv]; log_gamma [B,H,N]
  *   decode   q, k [B,H,dk];   v, out [B,H,dv];   log_gamma [B,H]
@@ -74,7 +76,9 @@ typedef enum {
                                  without being identical                      */
     GRET_ERR_HIP = 5,         /* a HIP runtime call or launch failed          */
     GRET_ERR_WORKSPACE = 6,   /* workspace missing, too small or misaligned   */
-    GRET_ERR_VALUE = 7        /* a scalar argument out of range (eps, scale)  */
+    GRET_ERR_VALUE = 7,       /* a scalar argument out of range (eps, scale)  */
+    GRET_ERR_SCRATCH = 8      /* gret_prefill_noalloc: the sizes need more than
+                                 its fixed device scratch                     */
 } gret_status_t;
 
 /* Log-gate floor used in place of -inf (gamma ~ 1.8e-35). */
@@ -130,6 +134,36 @@ int gret_prefill(const void* q, const void* k, const void* v, const float* log_g
                  const float* state_in, void* out, float* state_out, int64_t B, int64_t H,
                  int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, void* workspace,
                  size_t workspace_bytes, void* stream);
+
+/*
+ * gret_prefill_noalloc -- gret_prefill for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, semantics and results as gret_prefill,
+ * without the workspace: the bf16 path keeps its partial segment states in a
+ * device array of GRET_NOALLOC_SCRATCH_BYTES owned by the library, one per GPU,
+ * created when the library's code is loaded on that GPU and held until the
+ * process ends. The call allocates nothing (no hipMalloc, no allocating
+ * library routine); on its first call on a GPU it looks up that GPU's array
+ * with hipGetSymbolAddress (the caller's device must be current).
+ *
+ * Limit: the scratch must hold this device's segment plan, i.e. the number
+ * of bytes gret_prefill_workspace_bytes would give for the device's own number
+ * of workgroups (one per compute unit) instead of its device-independent cap.
+ * At dk = dv = 128 that is 64 KiB per segment; 24 heads of any length need
+ * about 19 MB on a 256-CU GPU. Larger requests return GRET_ERR_SCRATCH (before
+ * anything is enqueued, after a device-attribute query). fp32 calls need no
+ * scratch.
+ *
+ * Every call on one GPU shares that GPU's array, whose contents the kernels
+ * fully rewrite before reading (nothing needs clearing). Calls that overlap in
+ * time on one GPU -- on different streams, or from different threads without
+ * ordering -- race on it and give undefined results: order them on one stream.
+ */
+#define GRET_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gret_prefill_noalloc(const void* q, const void* k, const void* v, const float* log_gamma,
+                         const float* state_in, void* out, float* state_out, int64_t B, int64_t H,
+                         int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
+                         void* stream);
 
 /*
  * gret_decode_step -- one recurrent step for B*H independent heads.

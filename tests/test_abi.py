@@ -12,7 +12,7 @@ import yoco_gated_retention_amd as gret
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gret.h")
 
-OK, NULL, SHAPE, UNSUP, ALIAS, HIP, WORKSPACE, VALUE = range(8)
+OK, NULL, SHAPE, UNSUP, ALIAS, HIP, WORKSPACE, VALUE, SCRATCH = range(9)
 F32, BF16 = 0, 1
 
 
@@ -36,10 +36,11 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         assert gret.gret_status_string(s).startswith(
             ["GRET_OK", "GRET_ERR_NULL", "GRET_ERR_SHAPE", "GRET_ERR_UNSUPPORTED",
-             "GRET_ERR_ALIAS", "GRET_ERR_HIP", "GRET_ERR_WORKSPACE", "GRET_ERR_VALUE"][s])
+             "GRET_ERR_ALIAS", "GRET_ERR_HIP", "GRET_ERR_WORKSPACE", "GRET_ERR_VALUE",
+             "GRET_ERR_SCRATCH"][s])
     assert gret.gret_status_string(99) == "unknown gret status"
 
 
@@ -108,6 +109,23 @@ def test_prefill_aliasing(lib):
     assert prefill(lib, so=P(1)) == ALIAS
     # workspace on top of state_in
     assert prefill(lib, si=P(7), ws=P(7)) == ALIAS
+
+
+def test_prefill_noalloc_validation(lib):
+    # the variant without a workspace validates like gret_prefill and, for
+    # these rejected calls, returns before any HIP call
+    def call(q=P(0), out=P(4), so=P(5), si=None, B=1, H=2, N=512, dk=64, dv=64, chunk=64,
+             dtype=BF16):
+        return lib.gret_prefill_noalloc(q, P(1), P(2), P(3), si, out, so, B, H, N, dk, dv, chunk,
+                                        dtype, None)
+    assert call(q=None) == NULL
+    assert call(out=None) == NULL
+    assert call(N=0) == SHAPE
+    assert call(dk=32) == UNSUP
+    assert call(chunk=100) == UNSUP
+    assert call(dtype=3) == UNSUP
+    assert call(out=P(0)) == ALIAS
+    assert call(si=P(6), so=ctypes.c_void_p(BASE + 6 * 256 * MB + 4096)) == ALIAS
 
 
 def test_decode_validation(lib):

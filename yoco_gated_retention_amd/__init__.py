@@ -8,6 +8,8 @@ library is not built, every call raises.
 Functions mirror the C ABI names:
   gret_prefill(q, k, v, log_gamma, state_in=None, chunk=64, out=None,
                state_out=None, workspace=None) -> (out, state_out)
+  gret_prefill_noalloc(q, k, v, log_gamma, state_in=None, chunk=64, out=None,
+                       state_out=None) -> (out, state_out)
   gret_prefill_gated(q, k, v, log_gamma, gate, state_in=None, norm_weight=None,
                      norm_bias=None, norm_eps=1e-5, chunk=64, out=None,
                      state_out=None, workspace=None) -> (out, state_out)
@@ -71,6 +73,9 @@ def load_library():
         lib.gret_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci,
                                      vp, sz, vp]
         lib.gret_prefill.restype = ci
+        lib.gret_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                             i64, ci, vp]
+        lib.gret_prefill_noalloc.restype = ci
         lib.gret_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ci, vp]
         lib.gret_decode_step.restype = ci
         lib.gret_prefill_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci,
@@ -236,6 +241,32 @@ def gret_prefill(q, k, v, log_gamma, state_in=None, chunk=64, out=None, state_ou
                _ptr(workspace), ws_bytes, _stream(q.device))
     if st != GRET_OK:
         raise GretError(st, "gret_prefill")
+    return out, state_out
+
+
+def gret_prefill_noalloc(q, k, v, log_gamma, state_in=None, chunk=64, out=None, state_out=None):
+    """gret_prefill without a workspace, for callers that cannot allocate device
+    memory: the library's fixed per-GPU scratch (GRET_NOALLOC_SCRATCH_BYTES) holds
+    the partial states. Pass out and state_out to allocate nothing at all.
+    Calls that overlap in time on one GPU race on the scratch."""
+    lib = load_library()
+    B, H, N, dk, dv = _prefill_shapes(q, v)
+    dev = q.device
+    _check_tensors([("q", q, None, None), ("k", k, q.shape, q.dtype), ("v", v, None, q.dtype),
+                    ("log_gamma", log_gamma, (B, H, N), torch.float32),
+                    ("state_in", state_in, (B, H, dk, dv), torch.float32),
+                    ("out", out, (B, H, N, dv), q.dtype),
+                    ("state_out", state_out, (B, H, dk, dv), torch.float32)], dev)
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=dev)
+    if state_out is None:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    st = _call(dev, lib.gret_prefill_noalloc, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma),
+               _ptr(state_in), _ptr(out), _ptr(state_out), B, H, N, dk, dv, chunk, code,
+               _stream(dev))
+    if st != GRET_OK:
+        raise GretError(st, "gret_prefill_noalloc")
     return out, state_out
 
 

@@ -1,18 +1,48 @@
 // gret_api.cpp -- the C ABI of libgret: argument validation, aliasing rules,
 // prefill planning and dispatch to the kernels. Validation never touches the
-// HIP runtime, so a rejected call has no side effect at all.
+// HIP runtime (gret_prefill_noalloc's scratch-size check follows a device
+// attribute query), so a rejected call has no side effect at all.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/gret.h"
 #include "gret_internal.h"
+
+// Device scratch of gret_prefill_noalloc: one array per GPU, created when the
+// library's code object is loaded on that device and held until the process
+// ends. Host code never uses the array's name as an address (on the host it is
+// only a stand-in for the symbol); kernels get the per-device address found by
+// hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[GRET_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
 using gret::SegPlan;
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device `dev` (the current device), looked up
+// once per device; nullptr if the lookup fails.
+void* scratch_on(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
 
 constexpr int64_t kMaxElems = int64_t(1) << 50;  // guards size arithmetic
 // The bf16 prefill addresses one head's rows through 32-bit buffer offsets.
@@ -90,7 +120,8 @@ int check_epilogue(const void* gate, const float* w, const float* b, float eps, 
 int prefill_impl(const void* q, const void* k, const void* v, const float* log_gamma,
                  const float* state_in, const gret::OutputGate* epi, void* out, float* state_out,
                  int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
-                 int dtype, void* workspace, size_t workspace_bytes, void* stream);
+                 int dtype, void* workspace, size_t workspace_bytes, bool use_scratch,
+                 void* stream);
 int decode_impl(const void* q, const void* k, const void* v, const float* log_gamma,
                 const float* state_in, const gret::OutputGate* epi, void* out, float* state_out,
                 int64_t B, int64_t H, int64_t dk, int64_t dv, int dtype, void* stream);
@@ -116,7 +147,8 @@ namespace {
 int prefill_impl(const void* q, const void* k, const void* v, const float* log_gamma,
                  const float* state_in, const gret::OutputGate* epi, void* out, float* state_out,
                  int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
-                 int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                 int dtype, void* workspace, size_t workspace_bytes, bool use_scratch,
+                 void* stream) {
     if (!q || !k || !v || !log_gamma || !out) return GRET_ERR_NULL;
     int st = check_common(B, H, N, dk, dv, dtype);
     if (st != GRET_OK) return st;
@@ -135,7 +167,11 @@ int prefill_impl(const void* q, const void* k, const void* v, const float* log_g
         if (st != GRET_OK) return st;
     }
     if (epi && gret::output_gate_groups(BHN, N) > gret::kMaxGridGroups) return GRET_ERR_SHAPE;
-    const size_t need = workspace_need(B, H, N, dk, dv, chunk, dtype);
+    if (use_scratch) {
+        workspace = nullptr;  // the library's own scratch replaces it (below)
+        workspace_bytes = 0;
+    }
+    const size_t need = use_scratch ? 0 : workspace_need(B, H, N, dk, dv, chunk, dtype);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
         return GRET_ERR_WORKSPACE;
 
@@ -199,6 +235,15 @@ int prefill_impl(const void* q, const void* k, const void* v, const float* log_g
     int64_t G = static_cast<int64_t>(cus) * per_cu;
     if (G > gret::kMaxPrefillGroups) G = gret::kMaxPrefillGroups;
     const SegPlan plan = make_plan(B, H, N, chunk, G);
+    if (use_scratch) {
+        // the scratch holds the workspace of this device's plan (its number of
+        // workgroups), not of the device-independent cap
+        if (gret::bf16_workspace_layout(plan, dk, dv).bytes > GRET_NOALLOC_SCRATCH_BYTES)
+            return GRET_ERR_SCRATCH;
+        a.workspace = scratch_on(dev);
+        a.workspace_bytes = GRET_NOALLOC_SCRATCH_BYTES;
+        if (!a.workspace) return GRET_ERR_HIP;
+    }
     st = hip_status(gret::launch_prefill_bf16(a, plan));
     if (st != GRET_OK || !epi) return st;
     return hip_status(gret::launch_output_gate_bf16(ea));
@@ -276,6 +321,10 @@ const char* gret_status_string(int status) {
                    "gret_prefill_workspace_bytes() or not 256-byte aligned";
         case GRET_ERR_VALUE:
             return "GRET_ERR_VALUE: norm_eps is negative or not finite, or scale is not finite";
+        case GRET_ERR_SCRATCH:
+            return "GRET_ERR_SCRATCH: gret_prefill_noalloc needs more than its fixed device "
+                   "scratch (GRET_NOALLOC_SCRATCH_BYTES) for these sizes; use gret_prefill "
+                   "with a workspace";
         default: return "unknown gret status";
     }
 }
@@ -295,7 +344,15 @@ int gret_prefill(const void* q, const void* k, const void* v, const float* log_g
                  int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, void* workspace,
                  size_t workspace_bytes, void* stream) {
     return prefill_impl(q, k, v, log_gamma, state_in, nullptr, out, state_out, B, H, N, dk, dv,
-                        chunk, dtype, workspace, workspace_bytes, stream);
+                        chunk, dtype, workspace, workspace_bytes, false, stream);
+}
+
+int gret_prefill_noalloc(const void* q, const void* k, const void* v, const float* log_gamma,
+                         const float* state_in, void* out, float* state_out, int64_t B, int64_t H,
+                         int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
+                         void* stream) {
+    return prefill_impl(q, k, v, log_gamma, state_in, nullptr, out, state_out, B, H, N, dk, dv,
+                        chunk, dtype, nullptr, 0, true, stream);
 }
 
 int gret_prefill_gated(const void* q, const void* k, const void* v, const float* log_gamma,
@@ -310,7 +367,7 @@ int gret_prefill_gated(const void* q, const void* k, const void* v, const float*
     epi.eps = norm_eps;
     if (!gate) return GRET_ERR_NULL;
     return prefill_impl(q, k, v, log_gamma, state_in, &epi, out, state_out, B, H, N, dk, dv,
-                        chunk, dtype, workspace, workspace_bytes, stream);
+                        chunk, dtype, workspace, workspace_bytes, false, stream);
 }
 
 int gret_decode_step(const void* q, const void* k, const void* v, const float* log_gamma,
