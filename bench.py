@@ -349,7 +349,7 @@ def time_prefill_gated(dp, chunk, steps, warmup, dev, seed=3003):
 STREAM_LIB = os.path.join(ROOT, "yoco_gated_retention_amd", "libgret_stream.so")
 
 
-def bench_stream_ceiling(dp, reps=5):
+def bench_stream_ceiling(dp, reps=5, all_variants=None):
     """Measured HBM ceiling for the prefill's access mix: three read streams and
     one write stream of one workload-sized array each (the prefill's own q, k,
     v and output buffers), 16 bytes per lane, swept over the cache policy of
@@ -381,6 +381,7 @@ def bench_stream_ceiling(dp, reps=5):
         """Best variant overall and the best rate of each cache-policy pair."""
         moved = nbytes * (reads + (1 if write else 0))
         top, by_pol = None, {}
+        table = []
         for (nl, ns) in pols:
             for u in unrolls:
                 for w in per_cu:
@@ -388,9 +389,14 @@ def bench_stream_ceiling(dp, reps=5):
                     gbs = moved / (ms * 1e-3) / 1e9
                     key = "%s_loads+%s_stores" % ("nt" if nl else "default", "nt" if ns else "wb")
                     by_pol[key] = max(by_pol.get(key, 0.0), gbs)
+                    table.append([nl, ns, u, w, round(gbs, 1)])
                     if top is None or gbs > top["GB/s"]:
                         top = {"GB/s": gbs, "ms": ms, "nt_load": nl, "nt_store": ns, "unroll": u,
                                "workgroups_per_cu": w}
+        if all_variants is not None:
+            all_variants.append({"reads": reads, "write": write,
+                                 "columns": ["nt_load", "nt_store", "unroll", "wg_per_cu", "GB/s"],
+                                 "rows": table})
         return top, by_pol
 
     res = {"array_bytes": nbytes, "timing": "median of %d runs per variant" % reps,
@@ -963,7 +969,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=DEFAULT_CHUNK)
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "xattn", "proj", "swa"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "xattn", "proj", "swa", "stream"],
+                    default=None)
     ap.add_argument("--decode-reps", type=int, default=1)
     ap.add_argument("--skip-peaks", action="store_true",
                     help="skip the measured HBM stream ceiling and the library GEMM rate")
@@ -1019,6 +1026,19 @@ def main():
               "data": "synthetic (seeded; value distributions of the pages' gRet gate)"}
 
     result["host_cpu"] = cpu_info()
+    if args.only == "stream":
+        # the stream ceiling alone, every variant, on arrays of the 512K workload's size
+        import types
+
+        n = CONFIGS["prefill_512k"]["N"] * CONFIGS["prefill_512k"]["H"] * 128
+        arr = types.SimpleNamespace(**{x: torch.empty(n, dtype=torch.bfloat16, device=dev)
+                                       for x in ("q", "k", "v", "out")})
+        table = []
+        st = bench_stream_ceiling(arr, all_variants=table)
+        st["variants"] = table
+        result.update({"value": st["read3_write1"]["GB/s"], "unit": "GB/s",
+                       "config": {"workload": "stream_3read_1write_%d_bytes" % st["array_bytes"]},
+                       "measured_peaks": {"hbm_stream": st}})
     if args.only in (None, "prefill"):
         result.update(bench_prefill_legs(gret, dev, args))
 

@@ -443,13 +443,16 @@ struct Lds {
 
 // Issues this wavefront's share of the DMA of the tile at tile_pos into set X.
 // Every wavefront loads the 64 log-gates (the same bytes to the same place), so
-// that all wavefronts issue the same number of memory operations.
+// that all wavefronts issue the same number of memory operations. q is the
+// head's query descriptor, or a zero-size one for a tile whose outputs are not
+// computed (its loads then move no data but still count as operations).
 template <int DK, int DV, int X>
-__device__ inline void dma_tile(const Lds<DK, DV>& L, const HeadRsrc& hr, uint32_t tile_pos) {
+__device__ inline void dma_tile(const Lds<DK, DV>& L, const HeadRsrc& hr,
+                                const __amdgpu_buffer_rsrc_t& q, uint32_t tile_pos) {
     using c = C64<DK, DV>;
     const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < c::QB; ++i) dma_block<DK, kTileQ>(hr.q, L.q[X], w * c::QB + i, tile_pos);
+    for (int i = 0; i < c::QB; ++i) dma_block<DK, kTileQ>(q, L.q[X], w * c::QB + i, tile_pos);
 #pragma unroll
     for (int i = 0; i < c::QB; ++i) dma_block<DK, kTileK>(hr.k, L.k[X], w * c::QB + i, tile_pos);
 #pragma unroll
@@ -489,83 +492,93 @@ __device__ inline void wait_tile(int k) {
 // chunk's output goes (the head's output, or a zero-size range that drops it
 // while a segment only advances its state); it is flushed from V buffer
 // (X + 2) % 3 just before the DMA of tile k + 2 reuses that set.
+//
+// `full` says whether this chunk's outputs are computed (its queries were
+// loaded); otherwise the chunk only advances the state. The running log-decay
+// `total` (through the previous chunk) is advanced by this chunk's total;
+// `next_full` receives the mode of tile k + 2, whose DMA this chunk issues:
+// full when the caller asked for every output, or once the running log-decay
+// through this chunk is below kSurvivalDropLog.
 template <int DK, int DV, int X>
-__device__ inline float chunk(const Lds<DK, DV>& L, const HeadRsrc& hr,
-                              const __amdgpu_buffer_rsrc_t& prev_out, int k, uint32_t pos,
-                              Acc<DK, DV>& a) {
+__device__ inline void chunk(const Lds<DK, DV>& L, const HeadRsrc& hr,
+                             const __amdgpu_buffer_rsrc_t& prev_out,
+                             const __amdgpu_buffer_rsrc_t& no_q, int k, uint32_t pos, bool full,
+                             bool all_full, float& total, bool& next_full, Acc<DK, DV>& a) {
     using c = C64<DK, DV>;
     wait_tile<DK, DV>(k);
     if (threadIdx.x < 64) tables_from_lds(L.ell[X], L.tab[X]);
     lds_barrier();
-    if (k > 0) flush_tile<DK, DV>(L.v[(X + 2) % 3], prev_out, pos - kTile);
-    dma_tile<DK, DV, (X + 2) % 3>(L, hr, pos + 2 * kTile);
     const TileView tv{L.q[X], L.k[X], L.v[X], L.tab[X], L.tab[X] + 64, L.tab[X] + 128};
-    f32x4 o[c::CT][4];
-    cross_term<DK, DV>(tv, a, o);
-    scores_diag<DK, DV>(tv, L.ps);
-    lds_barrier();
-    apply_scores<DK, DV>(L.ps, tv.vs, o);
     const float gc = tv.beta[kTile - 1];
+    total += gc;
+    next_full = all_full || total < kSurvivalDropLog;
+    if (k > 0) flush_tile<DK, DV>(L.v[(X + 2) % 3], prev_out, pos - kTile);
+    dma_tile<DK, DV, (X + 2) % 3>(L, hr, next_full ? hr.q : no_q, pos + 2 * kTile);
+    f32x4 o[c::CT][4];
+    if (full) {
+        cross_term<DK, DV>(tv, a, o);
+        scores_diag<DK, DV>(tv, L.ps);
+        lds_barrier();
+        apply_scores<DK, DV>(L.ps, tv.vs, o);
+    }
     scale_state<DK, DV>(a, __expf(gc));
     state_update<DK, DV>(tv, a);
-    out_to_lds<DK, DV>(L.v[X], o);
-    return gc;
+    if (full) out_to_lds<DK, DV>(L.v[X], o);
 }
 
-// Runs chunks [cb, ce) of head x. With full_from_start the pass writes outputs
-// from the first chunk; otherwise only once the running log-decay has dropped
-// below kSurvivalDropLog (earlier outputs are computed but dropped). Returns
-// the total log-decay; *lead receives the number of output-free chunks. Reads
-// past the head's end return zeros, so the loop has no tail case; the loop is
-// unrolled by three so that every access's buffer set is a compile-time fact.
-template <int DK, int DV>
+// Runs chunks [cb, ce) of head x. With full_from_start the pass computes and
+// writes every output; otherwise a chunk's outputs are computed and written
+// only once the running log-decay before the previous chunk has dropped below
+// kSurvivalDropLog (the mode of a tile is fixed when its DMA is issued, two
+// chunks ahead; earlier chunks load no queries and only advance the state).
+// Returns the total log-decay; *lead receives the number of output-free
+// chunks. Reads past the head's end return zeros, so the loop has no tail
+// case; the loop is unrolled by three so that every access's buffer set is a
+// compile-time fact.
+// ALL_FULL compiles the pass that computes every output (the prefix launch)
+// without the mode bookkeeping.
+template <int DK, int DV, bool ALL_FULL = false>
 __device__ float run_chunks(const Params& p, const Lds<DK, DV>& L, int64_t x, int64_t cb,
-                            int64_t ce, bool full_from_start, Acc<DK, DV>& a, int64_t* lead) {
-    bool full = full_from_start;
+                           int64_t ce, bool full_from_start, Acc<DK, DV>& a, int64_t* lead) {
     float total = 0.0f;
-    *lead = full ? 0 : (ce - cb);
     const HeadRsrc hr = head_rsrc<DK, DV>(p, x);
+    // a zero-size range: stores through it are dropped, loads move no data
     const __amdgpu_buffer_rsrc_t drop = make_rsrc(p.out, 0);
     const int nch = static_cast<int>(ce - cb);
+    const bool all = ALL_FULL || full_from_start;
     uint32_t pos = static_cast<uint32_t>(cb * kTile);
     // earlier passes of this workgroup: drain their memory operations, and let
     // every wavefront finish reading the buffers
     wait_vm<0>();
     lds_barrier();
-    dma_tile<DK, DV, 0>(L, hr, pos);
-    dma_tile<DK, DV, 1>(L, hr, pos + kTile);
-    auto account = [&](float gc, int k) {
-        total += gc;
-        if (!full && total < kSurvivalDropLog) {
-            full = true;
-            *lead = k + 1;
-        }
+    // modes of the tiles in buffer sets 0, 1, 2
+    bool f0 = all, f1 = all, f2 = all;
+    dma_tile<DK, DV, 0>(L, hr, all ? hr.q : drop, pos);
+    dma_tile<DK, DV, 1>(L, hr, all ? hr.q : drop, pos + kTile);
+    int first_full = all ? 0 : nch;  // first chunk whose outputs are written
+    auto note = [&](bool f, int k) {
+        if (f && first_full > k) first_full = k;
     };
     __amdgpu_buffer_rsrc_t prev = drop;  // destination of the staged output
     int last = 0;                        // buffer set holding it
     for (int k = 0;; k += 3, pos += 3 * kTile) {
         if (k >= nch) break;
-        {
-            const __amdgpu_buffer_rsrc_t cur = full ? hr.out : drop;
-            account(chunk<DK, DV, 0>(L, hr, prev, k, pos, a), k);
-            prev = cur;
-            last = 0;
-        }
+        note(f0, k);
+        chunk<DK, DV, 0>(L, hr, prev, drop, k, pos, f0, all, total, f2, a);
+        prev = f0 ? hr.out : drop;
+        last = 0;
         if (k + 1 >= nch) break;
-        {
-            const __amdgpu_buffer_rsrc_t cur = full ? hr.out : drop;
-            account(chunk<DK, DV, 1>(L, hr, prev, k + 1, pos + kTile, a), k + 1);
-            prev = cur;
-            last = 1;
-        }
+        note(f1, k + 1);
+        chunk<DK, DV, 1>(L, hr, prev, drop, k + 1, pos + kTile, f1, all, total, f0, a);
+        prev = f1 ? hr.out : drop;
+        last = 1;
         if (k + 2 >= nch) break;
-        {
-            const __amdgpu_buffer_rsrc_t cur = full ? hr.out : drop;
-            account(chunk<DK, DV, 2>(L, hr, prev, k + 2, pos + 2 * kTile, a), k + 2);
-            prev = cur;
-            last = 2;
-        }
+        note(f2, k + 2);
+        chunk<DK, DV, 2>(L, hr, prev, drop, k + 2, pos + 2 * kTile, f2, all, total, f1, a);
+        prev = f2 ? hr.out : drop;
+        last = 2;
     }
+    *lead = first_full;
     // the last chunk's output: every wavefront's columns must be staged first
     lds_barrier();
     const uint32_t last_pos = static_cast<uint32_t>((ce - 1) * kTile);
@@ -630,7 +643,7 @@ __global__ __launch_bounds__(kThreadsFor<DV>) void prefill_prefix_c64_kernel(Par
     Acc<DK, DV> a;
     load_state<DK, DV>(a, p.ws_state + (x * pl.max_seg + slot) * (int64_t)(DK * DV));
     int64_t unused = 0;
-    run_chunks<DK, DV>(p, L, x, cb, cb + lead, true, a, &unused);
+    run_chunks<DK, DV, true>(p, L, x, cb, cb + lead, true, a, &unused);
 }
 #undef GRET_C64_LDS
 
