@@ -301,7 +301,8 @@ class DevicePrefill:
         torch.cuda.empty_cache()
 
 
-def prefill_roofline(B, H, N, dk, dv, chunk, state_in, ms, kernel, measured_gbs=None):
+def prefill_roofline(B, H, N, dk, dv, chunk, state_in, ms, kernel, measured_gbs=None,
+                     measured_seg_gbs=None):
     nbytes, flops = prefill_algorithmic(B, H, N, dk, dv, chunk, state_in)
     achieved = nbytes / (ms * 1e-3) / 1e9
     r = {"kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -311,6 +312,9 @@ def prefill_roofline(B, H, N, dk, dv, chunk, state_in, ms, kernel, measured_gbs=
     if measured_gbs:
         r["peak_measured"] = measured_gbs
         r["frac_measured"] = achieved / measured_gbs
+    if measured_seg_gbs:
+        r["peak_measured_segmented"] = measured_seg_gbs
+        r["frac_measured_segmented"] = achieved / measured_seg_gbs
     return r
 
 
@@ -353,9 +357,11 @@ def bench_stream_ceiling(dp, reps=5, all_variants=None):
     """Measured HBM ceiling for the prefill's access mix: three read streams and
     one write stream of one workload-sized array each (the prefill's own q, k,
     v and output buffers), 16 bytes per lane, swept over the cache policy of
-    loads and stores, rows per lane (unroll) and workgroups per CU; plus the
-    read-only, write-only and copy rates of the same kernels. Median of `reps`
-    runs per variant; the best variant of each mix is reported."""
+    loads and stores, rows per lane (unroll) and workgroups per CU; the same mix
+    in the prefill's own pattern (each CU streams its own contiguous segment,
+    loads through LDS); plus the read-only, write-only and copy rates of the
+    grid-stride kernels. Median of `reps` runs per variant; the best variant of
+    each mix is reported."""
     import ctypes
 
     import torch
@@ -364,6 +370,8 @@ def bench_stream_ceiling(dp, reps=5, all_variants=None):
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.gret_stream_run.argtypes = [ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, i64, vp]
     lib.gret_stream_run.restype = ci
+    lib.gret_stream_segmented_run.argtypes = [ci, ci, ci, ci, vp, vp, vp, vp, i64, vp]
+    lib.gret_stream_segmented_run.restype = ci
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     nbytes = dp.q.numel() * dp.q.element_size()
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
@@ -403,6 +411,25 @@ def bench_stream_ceiling(dp, reps=5, all_variants=None):
            "kernel": "stream_kernel (libgret_stream.so): 16 B per lane, grid-stride, persistent"}
     res["read3_write1"], res["read3_write1_by_policy"] = sweep(3, 1, [(1, 0), (0, 1), (0, 0),
                                                                       (1, 1)])
+    # the prefill's own pattern: one workgroup per CU streaming its own segment
+    # through LDS (one segment per CU, as the prefill's one workgroup per CU)
+    seg_rows, seg_top = [], None
+    for (nl, ns) in [(1, 0), (1, 1), (0, 0), (0, 1)]:
+        for depth in (2, 3, 4, 6):
+            def f(depth=depth, nl=nl, ns=ns):
+                rc = lib.gret_stream_segmented_run(depth, nl, ns, cus, a, b, c, o, nbytes, sp)
+                if rc != 0:
+                    raise RuntimeError("gret_stream_segmented_run failed: %d" % rc)
+            ms = time_calls(f, reps, 2)[1]
+            gbs = 4 * nbytes / (ms * 1e-3) / 1e9
+            seg_rows.append([nl, ns, depth, round(gbs, 1)])
+            if seg_top is None or gbs > seg_top["GB/s"]:
+                seg_top = {"GB/s": gbs, "ms": ms, "nt_load": nl, "nt_store": ns, "depth": depth,
+                           "workgroups": cus}
+    res["read3_write1_segmented"] = seg_top
+    if all_variants is not None:
+        all_variants.append({"reads": 3, "write": 1, "segmented": True,
+                             "columns": ["nt_load", "nt_store", "depth", "GB/s"], "rows": seg_rows})
     res["read3"] = sweep(3, 0, [(1, 0), (0, 0)])[0]
     res["copy"] = sweep(1, 1, [(1, 0), (0, 1), (0, 0), (1, 1)])[0]
     res["write"] = sweep(0, 1, [(0, 0), (0, 1)], unrolls=(4,))[0]
@@ -815,13 +842,15 @@ def bench_prefill_legs(gret, dev, args):
     peaks = {}
     if not args.skip_peaks:
         peaks["hbm_stream"] = bench_stream_ceiling(dp)
-        log("stream ceiling 3 reads + 1 write: %.0f GB/s (%s)" % (
-            peaks["hbm_stream"]["read3_write1"]["GB/s"],
-            json.dumps(peaks["hbm_stream"]["read3_write1_by_policy"])))
+        log("stream ceiling 3 reads + 1 write: %.0f GB/s (%s); segmented, through LDS: %.0f GB/s"
+            % (peaks["hbm_stream"]["read3_write1"]["GB/s"],
+               json.dumps(peaks["hbm_stream"]["read3_write1_by_policy"]),
+               peaks["hbm_stream"]["read3_write1_segmented"]["GB/s"]))
         peaks["bf16_gemm"] = bench_gemm_peak(dev)
         log("bf16 GEMM: %.0f TFLOP/s" % peaks["bf16_gemm"]["TFLOP/s"])
     meas = peaks["hbm_stream"]["read3_write1"]["GB/s"] if peaks else None
-    roof = prefill_roofline(B, H, N, dk, dv, chunk, False, ms, kern, meas)
+    meas_seg = peaks["hbm_stream"]["read3_write1_segmented"]["GB/s"] if peaks else None
+    roof = prefill_roofline(B, H, N, dk, dv, chunk, False, ms, kern, meas, meas_seg)
     roof["traffic"] = recorded_traffic("prefill")
     roof["mfma_busy_pct"] = recorded_mfma("prefill", "prefill_main_c64_kernel")
     if peaks:
@@ -835,8 +864,9 @@ def bench_prefill_legs(gret, dev, args):
         "roofline": roof, "measured_peaks": peaks or None})
     log("prefill chunk=%d: %.3f ms/step (median %.3f), %.3e tokens/s, %.0f GB/s (%.1f%% of HBM "
         "peak%s)" % (chunk, ms, med, res["value"], roof["achieved"], 100 * roof["frac"],
-                     "" if not meas else ", %.1f%% of the measured stream ceiling" %
-                     (100 * roof["frac_measured"])))
+                     "" if not meas else ", %.1f%% / %.1f%% of the measured grid-stride / "
+                     "segmented stream ceilings" % (100 * roof["frac_measured"],
+                                                    100 * roof["frac_measured_segmented"])))
 
     # gates near 1 (u ~ N(4, 1)), same q, k, v
     n_rep = max(10, args.steps // 2)
@@ -847,7 +877,8 @@ def bench_prefill_legs(gret, dev, args):
         "log_gamma": "u ~ N(4, 1), mean log-gate -0.0018 (gamma ~ 0.998), no sharp positions",
         "ms_median": med_slow, "tokens_per_s": B * N / (med_slow * 1e-3),
         "ratio_to_standard_median": med_slow / med,
-        "roofline": prefill_roofline(B, H, N, dk, dv, chunk, False, med_slow, kern, meas),
+        "roofline": prefill_roofline(B, H, N, dk, dv, chunk, False, med_slow, kern, meas,
+                                     meas_seg),
         "timing": "median of %d calls" % n_rep}
     log("prefill, gates near 1: %.3f ms (%.2fx the standard regime)" % (med_slow, med_slow / med))
     dp.set_log_gamma(d3["log_gamma"], dev)
@@ -857,7 +888,8 @@ def bench_prefill_legs(gret, dev, args):
     for ch in (64, 128, 256):
         _, m, _ = dp.time(ch, n_rep, 2)
         sweep.append({"chunk": ch, "ms_median": m, "tokens_per_s": B * N / (m * 1e-3),
-                      "roofline": prefill_roofline(B, H, N, dk, dv, ch, False, m, kern, meas)})
+                      "roofline": prefill_roofline(B, H, N, dk, dv, ch, False, m, kern, meas,
+                                                    meas_seg)})
         if ch != chunk:
             dp.ws.pop(ch, None)  # keep one workspace resident at a time
     res["prefill_512k_chunk_sweep"] = sweep
@@ -884,7 +916,7 @@ def bench_prefill_legs(gret, dev, args):
         _, m, _ = dp2.time(ch, 20, 3)
         sw2.append({"chunk": ch, "ms_median": m, "tokens_per_s": c2["N"] / (m * 1e-3),
                     "roofline": prefill_roofline(1, c2["H"], c2["N"], c2["dk"], c2["dv"], ch,
-                                                 False, m, kern, meas)})
+                                                 False, m, kern, meas, meas_seg)})
     dp2.free()
     res["prefill_32k_chunk_sweep"] = {"workload": c2["name"], "timing": "median of 20 calls",
                                       "chunks": sw2}
@@ -908,7 +940,7 @@ def bench_prefill_legs(gret, dev, args):
                          "ms_min": min(per4), "tokens_per_s": c4["N"] / (m4 * 1e-3),
                          "timing": "median of 10 calls",
                          "roofline": prefill_roofline(1, c4["H"], c4["N"], c4["dk"], c4["dv"],
-                                                      chunk, True, m4, kern, meas)}
+                                                      chunk, True, m4, kern, meas, meas_seg)}
     log("1M prefill: %.3f ms (%.1f%% of HBM peak)" % (
         m4, 100 * res["prefill_1m"]["roofline"]["frac"]))
 

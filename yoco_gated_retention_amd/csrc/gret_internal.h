@@ -14,13 +14,12 @@ constexpr float kLogGammaFloor = -80.0f;
 
 // A segment's incoming state S_in reaches output n of the segment as
 // exp(B_n) q_n S_in, B_n the log-decay accumulated since the segment start.
-// Once B_n < -32 (exp(-32) ~ 1.3e-14 ~ 2^-46) that term is below
-// 2^-46 |q_n|_1 max|S_in|: 22 bits under the fp32 resolution of an output on
-// the incoming state's own scale, and 37 bits under the bf16 rounding that the
-// cross-chunk product already applies to the state operand. From there on a
-// segment's outputs come from its zero-state pass; its leading chunks are
-// recomputed from S_in.
-constexpr float kSurvivalDropLog = -32.0f;
+// Once B_n < -20 (exp(-20) ~ 2.1e-9 ~ 2^-28.9) that term is below
+// 2^-28 |q_n|_1 max|S_in|: about 19 bits under the bf16 rounding of a stored
+// output on the incoming state's own scale, and of the bf16 state operand the
+// cross-chunk product itself uses. From there on a segment's outputs come from
+// its zero-state pass; its leading chunks are recomputed from S_in.
+constexpr float kSurvivalDropLog = -20.0f;
 
 // Workgroups one launch may have (a single grid dimension). The C ABI checks
 // every launch of a call against it before anything is enqueued.

@@ -439,16 +439,19 @@ struct Lds {
     float* ell[3];
     float* tab[3];  // beta[64] | gam[64] | fexp[64]
     bf16_t* ps;
+    float* sink;    // target of the log-gate DMA of wavefronts other than 0
 };
 
 // Issues this wavefront's share of the DMA of the tile at tile_pos into set X.
-// Every wavefront loads the 64 log-gates (the same bytes to the same place), so
-// that all wavefronts issue the same number of memory operations. q is the
-// head's query descriptor, or a zero-size one for a tile whose outputs are not
-// computed (its loads then move no data but still count as operations).
+// Wavefront 0 loads the 64 log-gates; the others issue the same instruction
+// through a zero-size descriptor into a sink (no data moves), so that all
+// wavefronts issue the same number of memory operations. q is the head's query
+// descriptor, or a zero-size one for a tile whose outputs are not computed
+// (its loads then move no data but still count as operations).
 template <int DK, int DV, int X>
 __device__ inline void dma_tile(const Lds<DK, DV>& L, const HeadRsrc& hr,
-                                const __amdgpu_buffer_rsrc_t& q, uint32_t tile_pos) {
+                                const __amdgpu_buffer_rsrc_t& q,
+                                const __amdgpu_buffer_rsrc_t& none, uint32_t tile_pos) {
     using c = C64<DK, DV>;
     const int w = threadIdx.x >> 6;
 #pragma unroll
@@ -457,7 +460,9 @@ __device__ inline void dma_tile(const Lds<DK, DV>& L, const HeadRsrc& hr,
     for (int i = 0; i < c::QB; ++i) dma_block<DK, kTileK>(hr.k, L.k[X], w * c::QB + i, tile_pos);
 #pragma unroll
     for (int i = 0; i < c::VB; ++i) dma_block<DV, kTileV>(hr.v, L.v[X], w * c::VB + i, tile_pos);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(hr.lg, (lds_void*)L.ell[X], 4,
+    const bool w0 = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) == 0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(w0 ? hr.lg : none,
+                                             (lds_void*)(w0 ? L.ell[X] : L.sink), 4,
                                              (tile_pos + (threadIdx.x & 63)) * 4, 0, 0,
                                              kStreamLoad);
 }
@@ -513,7 +518,7 @@ __device__ inline void chunk(const Lds<DK, DV>& L, const HeadRsrc& hr,
     total += gc;
     next_full = all_full || total < kSurvivalDropLog;
     if (k > 0) flush_tile<DK, DV>(L.v[(X + 2) % 3], prev_out, pos - kTile);
-    dma_tile<DK, DV, (X + 2) % 3>(L, hr, next_full ? hr.q : no_q, pos + 2 * kTile);
+    dma_tile<DK, DV, (X + 2) % 3>(L, hr, next_full ? hr.q : no_q, no_q, pos + 2 * kTile);
     f32x4 o[c::CT][4];
     if (full) {
         cross_term<DK, DV>(tv, a, o);
@@ -553,8 +558,8 @@ __device__ float run_chunks(const Params& p, const Lds<DK, DV>& L, int64_t x, in
     lds_barrier();
     // modes of the tiles in buffer sets 0, 1, 2
     bool f0 = all, f1 = all, f2 = all;
-    dma_tile<DK, DV, 0>(L, hr, all ? hr.q : drop, pos);
-    dma_tile<DK, DV, 1>(L, hr, all ? hr.q : drop, pos + kTile);
+    dma_tile<DK, DV, 0>(L, hr, all ? hr.q : drop, drop, pos);
+    dma_tile<DK, DV, 1>(L, hr, all ? hr.q : drop, drop, pos + kTile);
     int first_full = all ? 0 : nch;  // first chunk whose outputs are written
     auto note = [&](bool f, int k) {
         if (f && first_full > k) first_full = k;
@@ -600,8 +605,9 @@ __device__ float run_chunks(const Params& p, const Lds<DK, DV>& L, int64_t x, in
     __shared__ __attribute__((aligned(16))) float t0_[3 * kTile], t1_[3 * kTile],        \
         t2_[3 * kTile];                                                                   \
     __shared__ __attribute__((aligned(16))) bf16_t ps_[kTile * C64<DK, DV>::PP];          \
+    __shared__ __attribute__((aligned(16))) float sink_[kTile];                           \
     const Lds<DK, DV> L{{q0_, q1_, q2_}, {k0_, k1_, k2_}, {v0_, v1_, v2_},                \
-                        {l0_, l1_, l2_}, {t0_, t1_, t2_}, ps_};
+                        {l0_, l1_, l2_}, {t0_, t1_, t2_}, ps_, sink_};
 
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreadsFor<DV>) void prefill_main_c64_kernel(Params p) {

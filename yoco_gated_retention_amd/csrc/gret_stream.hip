@@ -10,6 +10,12 @@
 // or nontemporal), rows per lane and iteration (U), and workgroups per
 // compute unit (the grid is persistent: CUs x W workgroups of 256 threads
 // walk the arrays with a grid stride).
+//
+// The segmented form mirrors the prefill's own memory pattern: each of G
+// workgroups (8 wavefronts, one per compute unit) streams its own contiguous
+// 1/G of the arrays, the loads go from HBM straight into LDS with
+// buffer_load ... lds, D 1 KB blocks per stream and wavefront in flight, and
+// the output leaves from LDS through the registers with 16-byte stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -95,6 +101,80 @@ __global__ __launch_bounds__(256) void fill_kernel(i32x4* __restrict__ o, int64_
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int vm_wait_imm(int n) {
+    return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8);
+}
+template <int N>
+__device__ inline void wait_vm() {
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(N));
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Segmented 3-read/1-write stream through LDS: D iterations in flight per
+// wavefront; at least 96 KB of LDS per workgroup, so one workgroup per CU.
+template <int D, int POL_L, int POL_S>
+__global__ __launch_bounds__(512) void seg_stream_kernel(const char* a, const char* b,
+                                                         const char* c, char* o, int64_t nblk) {
+    constexpr int kSlots = D < 4 ? 4 : D;
+    __shared__ __attribute__((aligned(16))) char lds[8 * kSlots * 3072];
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * nblk / gridDim.x;
+    const int64_t hi = static_cast<int64_t>(blockIdx.x + 1) * nblk / gridDim.x;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    char* mine = lds + w * D * 3072;
+    const int64_t nit = (hi - lo + 7) / 8;
+    const uint32_t sbytes = static_cast<uint32_t>((hi - lo) * 1024);
+    const __amdgpu_buffer_rsrc_t ra = rsrc(a + lo * 1024, sbytes), rb = rsrc(b + lo * 1024, sbytes),
+                                 rc = rsrc(c + lo * 1024, sbytes), ro = rsrc(o + lo * 1024, sbytes);
+    auto issue = [&](int64_t it, int slot) {
+        const uint32_t off = static_cast<uint32_t>((it * 8 + w) * 1024 + lane * 16);
+        char* d = mine + slot * 3072;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(d), 16, off, 0, 0, POL_L);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(d + 1024), 16, off, 0, 0, POL_L);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void*)(d + 2048), 16, off, 0, 0, POL_L);
+    };
+    // iterations past the segment read zeros and store nothing (range checks)
+#pragma unroll
+    for (int i = 0; i < D; ++i) issue(i, i);
+    for (int64_t it = 0; it < nit; it += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            // operations younger than iteration it+s's loads: in the prologue at
+            // least 3 (D-1) loads, afterwards (D-1) x (3 loads + 1 store)
+            if (it == 0)
+                wait_vm<(D - 1) * 3>();
+            else
+                wait_vm<(D - 1) * 4>();
+            const i32x4* p = reinterpret_cast<const i32x4*>(mine + s * 3072 + lane * 16);
+            const i32x4 v = p[0] ^ p[64] ^ p[128];
+            const uint32_t off = static_cast<uint32_t>(((it + s) * 8 + w) * 1024 + lane * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, POL_S);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): slot read before it is refilled
+            issue(it + s + D, s);
+        }
+    }
+    wait_vm<0>();
+}
+
+template <int D>
+hipError_t launch_seg(int nt_load, int nt_store, int groups, const void* a, const void* b,
+                      const void* c, void* o, int64_t nblk, hipStream_t s) {
+    auto A = static_cast<const char*>(a);
+    auto B = static_cast<const char*>(b);
+    auto C = static_cast<const char*>(c);
+    auto O = static_cast<char*>(o);
+    const dim3 g(groups), t(512);
+    if (nt_load && nt_store) hipLaunchKernelGGL((seg_stream_kernel<D, 2, 2>), g, t, 0, s, A, B, C, O, nblk);
+    else if (nt_load) hipLaunchKernelGGL((seg_stream_kernel<D, 2, 0>), g, t, 0, s, A, B, C, O, nblk);
+    else if (nt_store) hipLaunchKernelGGL((seg_stream_kernel<D, 0, 2>), g, t, 0, s, A, B, C, O, nblk);
+    else hipLaunchKernelGGL((seg_stream_kernel<D, 0, 0>), g, t, 0, s, A, B, C, O, nblk);
+    return hipGetLastError();
+}
+
 template <int R, bool W_OUT, bool NL, bool NS>
 hipError_t launch_u(int u, int groups, const void* a, const void* b, const void* c, void* o,
                     int64_t n16, hipStream_t s) {
@@ -159,6 +239,27 @@ int gret_stream_run(int reads, int write, int nt_load, int nt_store, int unroll,
         return write ? launch_pol<3, true>(nt_load, nt_store, unroll, groups, a, b, c, out, n16, s)
                      : launch_pol<3, false>(nt_load, nt_store, unroll, groups, a, b, c, out, n16, s);
     return hipErrorInvalidValue;
+}
+
+// The segmented form: `groups` workgroups each stream their own contiguous
+// 1/groups of three input arrays into one output array (bytes each, a multiple
+// of 1 KB, each workgroup's share below 4 GB), `depth` in {2, 3, 4, 6}.
+int gret_stream_segmented_run(int depth, int nt_load, int nt_store, int groups, const void* a,
+                              const void* b, const void* c, void* out, int64_t bytes,
+                              void* stream) {
+    if (bytes <= 0 || bytes % 1024 != 0 || groups < 1 || !a || !b || !c || !out)
+        return hipErrorInvalidValue;
+    const int64_t nblk = bytes / 1024;
+    // every offset a workgroup forms (its share plus the blocks issued past it)
+    if ((nblk / groups + 64) * 1024 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (depth) {
+        case 2: return launch_seg<2>(nt_load, nt_store, groups, a, b, c, out, nblk, s);
+        case 3: return launch_seg<3>(nt_load, nt_store, groups, a, b, c, out, nblk, s);
+        case 4: return launch_seg<4>(nt_load, nt_store, groups, a, b, c, out, nblk, s);
+        case 6: return launch_seg<6>(nt_load, nt_store, groups, a, b, c, out, nblk, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // extern "C"
