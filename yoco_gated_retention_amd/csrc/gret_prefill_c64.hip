@@ -357,16 +357,32 @@ __device__ inline void out_to_lds(bf16_t* vs, const f32x4 (&o)[C64<DK, DV>::CT][
         }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront: shifts by 1, 2, 4 and 8
+// lanes inside each 16-lane row, then the row totals carried across rows by the
+// row broadcasts of lanes 15 and 31 (DPP moves: no LDS crossbar round trips).
+// Lanes with no source add the identity 0.
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_or_zero(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, ROW_MASK, 0xF, false));
+}
+
+__device__ inline float wave_inclusive_sum(float x) {
+    constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+    x += dpp_or_zero<kRowShr | 1, 0xF>(x);
+    x += dpp_or_zero<kRowShr | 2, 0xF>(x);
+    x += dpp_or_zero<kRowShr | 4, 0xF>(x);
+    x += dpp_or_zero<kRowShr | 8, 0xF>(x);
+    x += dpp_or_zero<kRowBcast15, 0xA>(x);
+    x += dpp_or_zero<kRowBcast31, 0xC>(x);
+    return x;
+}
+
 // Wavefront 0: chunk tables from the log-gates in LDS (past the end they read 0).
 __device__ inline void tables_from_lds(const float* ell, float* tab) {
     const int lane = threadIdx.x;
-    float b = clamp_log_gamma(ell[lane], kLogGammaFloor);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(b, off);
-        if (lane >= off) b += o;
-    }
-    const float gc = __shfl(b, 63);
+    const float b = wave_inclusive_sum(clamp_log_gamma(ell[lane], kLogGammaFloor));
+    const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
     tab[lane] = b;
     tab[64 + lane] = __expf(gc - b);
     tab[128 + lane] = __expf(b);
@@ -449,15 +465,27 @@ struct Lds {
 // descriptor, or a zero-size one for a tile whose outputs are not computed
 // (its loads then move no data but still count as operations).
 template <int DK, int DV, int X>
-__device__ inline void dma_tile(const Lds<DK, DV>& L, const HeadRsrc& hr,
-                                const __amdgpu_buffer_rsrc_t& q,
-                                const __amdgpu_buffer_rsrc_t& none, uint32_t tile_pos) {
+__device__ inline void dma_q(const Lds<DK, DV>& L, const __amdgpu_buffer_rsrc_t& q,
+                             uint32_t tile_pos) {
     using c = C64<DK, DV>;
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < c::QB; ++i) dma_block<DK, kTileQ>(q, L.q[X], w * c::QB + i, tile_pos);
+}
+
+template <int DK, int DV, int X>
+__device__ inline void dma_k(const Lds<DK, DV>& L, const HeadRsrc& hr, uint32_t tile_pos) {
+    using c = C64<DK, DV>;
+    const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < c::QB; ++i) dma_block<DK, kTileK>(hr.k, L.k[X], w * c::QB + i, tile_pos);
+}
+
+template <int DK, int DV, int X>
+__device__ inline void dma_v_ell(const Lds<DK, DV>& L, const HeadRsrc& hr,
+                                 const __amdgpu_buffer_rsrc_t& none, uint32_t tile_pos) {
+    using c = C64<DK, DV>;
+    const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < c::VB; ++i) dma_block<DV, kTileV>(hr.v, L.v[X], w * c::VB + i, tile_pos);
     const bool w0 = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) == 0;
@@ -465,6 +493,15 @@ __device__ inline void dma_tile(const Lds<DK, DV>& L, const HeadRsrc& hr,
                                              (lds_void*)(w0 ? L.ell[X] : L.sink), 4,
                                              (tile_pos + (threadIdx.x & 63)) * 4, 0, 0,
                                              kStreamLoad);
+}
+
+template <int DK, int DV, int X>
+__device__ inline void dma_tile(const Lds<DK, DV>& L, const HeadRsrc& hr,
+                                const __amdgpu_buffer_rsrc_t& q,
+                                const __amdgpu_buffer_rsrc_t& none, uint32_t tile_pos) {
+    dma_q<DK, DV, X>(L, q, tile_pos);
+    dma_k<DK, DV, X>(L, hr, tile_pos);
+    dma_v_ell<DK, DV, X>(L, hr, none, tile_pos);
 }
 
 // Stores the output tile staged in a V buffer. Each wavefront flushes exactly
@@ -517,12 +554,19 @@ __device__ inline void chunk(const Lds<DK, DV>& L, const HeadRsrc& hr,
     const float gc = tv.beta[kTile - 1];
     total += gc;
     next_full = all_full || total < kSurvivalDropLog;
-    if (k > 0) flush_tile<DK, DV>(L.v[(X + 2) % 3], prev_out, pos - kTile);
-    dma_tile<DK, DV, (X + 2) % 3>(L, hr, next_full ? hr.q : no_q, no_q, pos + 2 * kTile);
+    // The DMA of tile k + 2 is issued in three parts spread over the chunk
+    // (queries, keys, then values and log-gates, always in that order), so that
+    // the eight wavefronts' memory instructions do not queue up behind each
+    // other at the start of the chunk.
+    constexpr int Y = (X + 2) % 3;
+    if (k > 0) flush_tile<DK, DV>(L.v[Y], prev_out, pos - kTile);
+    dma_q<DK, DV, Y>(L, next_full ? hr.q : no_q, pos + 2 * kTile);
     f32x4 o[c::CT][4];
+    if (full) cross_term<DK, DV>(tv, a, o);
+    dma_k<DK, DV, Y>(L, hr, pos + 2 * kTile);
+    if (full) scores_diag<DK, DV>(tv, L.ps);
+    dma_v_ell<DK, DV, Y>(L, hr, no_q, pos + 2 * kTile);
     if (full) {
-        cross_term<DK, DV>(tv, a, o);
-        scores_diag<DK, DV>(tv, L.ps);
         lds_barrier();
         apply_scores<DK, DV>(L.ps, tv.vs, o);
     }
