@@ -28,12 +28,6 @@ namespace {
 
 constexpr int kEpiThreads = 256;
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer, gfx9-family data format
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
-}
 __device__ inline i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }

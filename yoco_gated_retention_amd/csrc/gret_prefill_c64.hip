@@ -388,27 +388,6 @@ __device__ inline void tables_from_lds(const float* ell, float* tab) {
     tab[128 + lane] = __expf(b);
 }
 
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wavefront are outstanding (gfx9 encoding; expcnt and lgkmcnt left alone).
-constexpr int vm_wait_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
-constexpr int kLgkmWaitZero = 0xC07F;  // lgkmcnt(0) only
-
-template <int N>
-__device__ inline void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(N));
-}
-
-// Workgroup barrier for LDS data: this wavefront's LDS writes complete, then
-// s_barrier; compiler-only fences keep memory accesses on their side. Unlike
-// __syncthreads it carries no release fence, so it does not drain the loads
-// still in flight for later tiles.
-__device__ inline void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(kLgkmWaitZero);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // Cache policy of the streamed q/k/v/log-gate loads: nontemporal (each byte is
 // read once). The output stores keep the default write-back policy: with the

@@ -15,45 +15,12 @@ namespace {
 constexpr int kTile = 64;  // positions per tile
 constexpr int kPadP = 8;   // bf16 padding per row of the score tile
 
-// v_mfma_f32_16x16x32_bf16. Operand lanes: A row (B column) = lane % 16, the
-// 8 k-values of a lane are 8 (lane / 16) .. +7; C column = lane % 16, rows
-// 4 (lane / 16) .. +3.
-__device__ inline f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ inline bf16x8 lds_read8(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-__device__ inline bf16x4 lds_read4(const bf16_t* p) { return *reinterpret_cast<const bf16x4*>(p); }
-
-// Transposing LDS read: within each 16-lane group, lane l receives element
-// (l % 4) of the 8-byte pieces addressed by lanes 4e + l/4 (e = 0..3). With
-// lane s pointing at row t0 + s/4, column n0 + 4(s % 4) of a row-major tile,
-// lane l gets column n0 + l of rows t0..t0+3.
-__device__ inline bf16x4 lds_read_tr4(const bf16_t* p) {
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-    return __builtin_bit_cast(bf16x4, v);
-}
-
-__device__ inline bf16x8 cat44(const bf16x4& a, const bf16x4& b) {
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
 
 // Range-checked buffer access (CDNA buffer resources). A descriptor covers one
 // head's rows; a load past its end returns zeros and a store past it is
 // dropped by the hardware, which is exactly the tail masking the chunkwise form
 // needs (padded positions carry zero K and V and log-gate 0, and their outputs
 // are not written), without a branch on the hot path.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer, gfx9-family data format
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
-}
 __device__ inline bf16x8 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
     return __builtin_bit_cast(bf16x8, v);

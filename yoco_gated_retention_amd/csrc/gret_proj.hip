@@ -41,34 +41,6 @@ constexpr int kPStage = (kPN + kPM) * kPK;  // bf16 per stage: weight rows, then
 constexpr int kPGroupM = 6;     // token tiles per group of the workgroup order
 constexpr int kXcds = 8;
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer, gfx9-family data format
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
-}
-
-// v_mfma_f32_16x16x32_bf16: A row / B column = lane % 16 with k-values
-// 8 (lane / 16) .. +7; C column = lane % 16, rows 4 (lane / 16) .. +3.
-__device__ inline f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-constexpr int vm_wait_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
-template <int N>
-__device__ inline void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(N));
-}
-constexpr int kLgkmWaitZero = 0xC07F;
-
-__device__ inline void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(kLgkmWaitZero);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // Stage layout: rows of 32 bf16 (four 16-byte chunks); chunk c of row r sits
 // in slot c ^ ((r >> 1) & 3). Eight lanes reading one chunk of rows r0..r0+7

@@ -36,51 +36,6 @@ constexpr int kSK = 64;            // keys per LDS stage
 constexpr int kSStages = 3;        // LDS stages (3 or 4), filled kSStages - 1 blocks ahead
 constexpr int kXcds = 8;
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer, gfx9-family data format
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
-}
-
-// v_mfma_f32_32x32x16_bf16: A row / B column = lane % 32 with contraction
-// index 8 (lane / 32) + e for element e; C column = lane % 32, register r holds
-// row 8 (r / 4) + 4 (lane / 32) + r % 4.
-__device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ inline bf16x8 lds_read8(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-
-// Transposing LDS read: within each 16-lane group, lane l receives element
-// (l % 4) of the 8-byte pieces addressed by lanes 4e + l / 4 (e = 0..3). With
-// lane s pointing at row t0 + s / 4, column n0 + 4 (s % 4) of a row-major
-// tile, lane l gets column n0 + l of rows t0..t0+3.
-__device__ inline bf16x4 lds_read_tr4(const bf16_t* p) {
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-    return __builtin_bit_cast(bf16x4, v);
-}
-__device__ inline bf16x8 cat44(const bf16x4& a, const bf16x4& b) {
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-constexpr int vm_wait_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
-template <int N>
-__device__ inline void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(N));
-}
-constexpr int kLgkmWaitZero = 0xC07F;
-__device__ inline void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(kLgkmWaitZero);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // Tile layouts: row-major, the 16-byte chunks of row r permuted by c ^ sw(r).
 // K is read as 16-byte row pieces of 8 consecutive rows (any 8 aligned rows

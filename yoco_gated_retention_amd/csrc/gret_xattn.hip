@@ -38,29 +38,6 @@ constexpr int kXTile = 32;     // positions per tile
 constexpr int kXWaves = 4;     // wavefronts per workgroup
 constexpr int kXThreads = 64 * kXWaves;
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ inline f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ inline bf16x8 lds_read8(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-// Transposing LDS read: lane s of a 16-lane group points at row t0 + s/4,
-// column n0 + 4 (s % 4); lane l receives column n0 + l of rows t0..t0+3.
-__device__ inline bf16x4 lds_read_tr4(const bf16_t* p) {
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-    return __builtin_bit_cast(bf16x4, v);
-}
-__device__ inline bf16x8 cat44(const bf16x4& a, const bf16x4& b) {
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer, gfx9-family data format
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
-}
 
 // Tile layouts (row-major, 16-byte chunks of row r permuted by c ^ sigma(r));
 // K is read as 16-byte row fragments, V with the transposing load.
@@ -78,14 +55,6 @@ __device__ inline int xoff(int row, int col) {
     return row * D + (((col >> 3) ^ xswz<D, IS_V>(row)) << 3) + (col & 7);
 }
 
-// s_waitcnt for "at most n vector-memory operations outstanding" (gfx9 encoding).
-constexpr int vm_wait_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
-template <int N>
-__device__ inline void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(N));
-}
-constexpr int kLgkmWaitZero = 0xC07F;
 
 // One 1 KB DMA instruction of a tile with D columns (lane i -> LDS byte 16 i of
 // block blk = row (512/D) blk + i / (D/8), slot i % (D/8)).
