@@ -45,10 +45,9 @@ def _attend(qv, ks, vs, scale):
     return (p / p.sum()) @ vs
 
 
-def oracle_swa_prefill_f64(q, k, v, window, scale=None, block=256):
-    """Sliding-window causal attention of every query position (float64).
-    Query rows are processed in blocks of `block` against the keys of their
-    joint window, masked to each row's own window."""
+def oracle_swa_prefill_f64(q, k, v, window, scale=None):
+    """Sliding-window causal attention of every query position (float64), one
+    query row at a time over the keys of its own window."""
     qd, kd, vd = _widen(q), _widen(k), _widen(v)
     B, Hq, N, d = qd.shape
     _, Hkv, Nk, dk = kd.shape
@@ -63,16 +62,9 @@ def oracle_swa_prefill_f64(q, k, v, window, scale=None, block=256):
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            for i0 in range(0, N, block):
-                i1 = min(N, i0 + block)
-                j0 = max(0, i0 - window + 1)
-                s = scale * (qd[b, h, i0:i1] @ kd[b, g, j0:i1].T)   # [rows, keys]
-                ii = np.arange(i0, i1)[:, None]
-                jj = np.arange(j0, i1)[None, :]
-                s = np.where((jj <= ii) & (jj > ii - window), s, -np.inf)
-                s = s - s.max(axis=1, keepdims=True)
-                p = np.exp(s)
-                out[b, h, i0:i1] = (p / p.sum(axis=1, keepdims=True)) @ vd[b, g, j0:i1]
+            for i in range(N):
+                j0 = max(0, i - window + 1)
+                out[b, h, i] = _attend(qd[b, h, i], kd[b, g, j0:i + 1], vd[b, g, j0:i + 1], scale)
     return out
 
 

@@ -34,7 +34,7 @@ def test_prefill_matches_torch_window_mask(N, window, Hq, Hkv):
     q = rng.standard_normal((2, Hq, N, d))
     k = rng.standard_normal((2, Hkv, N, d))
     v = rng.standard_normal((2, Hkv, N, d))
-    got = oracle_swa_prefill_f64(q, k, v, window, block=7)
+    got = oracle_swa_prefill_f64(q, k, v, window)
     np.testing.assert_allclose(got, sdpa_window(q, k, v, window), rtol=1e-10, atol=1e-12)
 
 
