@@ -21,7 +21,9 @@
 // transpose leaves each lane with 4 consecutive channels of one token, which
 // are stored as one 8-byte piece straight into the head-major key layout. The
 // gate is one extra tile (weight rows past H read as zeros) spread over all
-// four wavefronts by tokens. Workgroups are ordered so that the tiles running
+// four wavefronts by tokens. The key tile's results leave through LDS (the
+// stage buffers, free once the last operands are read) so that every store
+// writes whole 16-byte pieces, 256 contiguous bytes per token and head. Workgroups are ordered so that the tiles running
 // together on one XCD share token tiles (x rows) and channel tiles (weight
 // rows) in that XCD's L2.
 #include <hip/hip_runtime.h>
@@ -244,22 +246,40 @@ __device__ inline void key_tile(const ProjParams& p, int64_t m0, int ct) {
     f32x4 acc[8][8];
     tile_loop<8, 8>(static_cast<int>(D / kPK), wn * kPWave, wm * kPWave, rw, rx, D, acc);
 
+    // Epilogue through LDS. Once every wavefront has read its last operands
+    // the four stage buffers are free: wavefront w stages its scaled bf16
+    // 128 x 128 tile token-major in buffer w (row t = 128 channels; 16-byte
+    // piece c of row t at slot c ^ (t % 16), so the 16 tokens of one product
+    // block land in 16 different slots), then stores whole 16-byte pieces:
+    // 16 lanes cover the 256 bytes of one token's channels.
+    lds_barrier();
+    bf16_t* st = wave == 0 ? proj_s0 : wave == 1 ? proj_s1 : wave == 2 ? proj_s2 : proj_s3;
     const int li = lane & 15, cq = 4 * (lane >> 4);
-    TokenMap tok[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tok[j] = token_at(p, m0 + wm * kPWave + 16 * j + li);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t jc = j0 + wn * kPWave + 16 * i + cq;
-        if (jc >= J) continue;  // J and jc are multiples of 4
-        const int64_t h = jc / p.dk, c = jc - h * p.dk;
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            if (!tok[j].ok) continue;
             bf16x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = to_bf16(acc[i][j][e] * p.key_scale);
-            *reinterpret_cast<bf16x4*>(p.k_out + ((tok[j].b * p.H + h) * p.N + tok[j].n) * p.dk + c) = v;
+            const int t = 16 * j + li, ch = 16 * i + cq;
+            *reinterpret_cast<bf16x4*>(st + t * kPWave + (((ch >> 3) ^ li) << 3) + (ch & 7)) = v;
+        }
+    const int c16 = lane & 15;
+    const int64_t jc = j0 + wn * kPWave + 8 * c16;  // first of this lane's 8 channels
+    const int64_t h = jc / p.dk, c = jc - h * p.dk;  // dk % 8 == 0: one head
+    const int64_t tw = m0 + wm * kPWave + (lane >> 4);
+    int64_t b = tw / p.N, n = tw - b * p.N;
+    bf16_t* dst_h = p.k_out + h * p.N * p.dk + c;
+    for (int s4 = 0; s4 < kPWave / 4; ++s4) {
+        const int t = 4 * s4 + (lane >> 4);
+        const bf16x8 val = *reinterpret_cast<const bf16x8*>(st + t * kPWave + ((c16 ^ (t & 15)) << 3));
+        if (tw + 4 * s4 < p.M && jc < J)
+            *reinterpret_cast<bf16x8*>(dst_h + (b * p.H * p.N + n) * p.dk) = val;
+        n += 4;
+        while (n >= p.N) {
+            n -= p.N;
+            ++b;
         }
     }
 }
