@@ -10,10 +10,12 @@
 //
 // The kernel is a streaming pass (read the row and its gate, write the row),
 // bound by HBM bandwidth: 3 * dv * sizeof(T) bytes per row. A workgroup takes
-// 64 consecutive rows of one head, so the head's affine for a lane's channels
+// 128 consecutive rows of one head, so the head's affine for a lane's channels
 // is loaded once; each lane owns one 16-byte piece of a row, a row is spread
 // over dv * sizeof(T) / 16 adjacent lanes, and a wavefront issues the loads of
-// all its rows before any arithmetic. Rows past N are handled by range-checked
+// all its rows (8 row pieces and their gates per lane at dv = 128 in bf16)
+// before any arithmetic. The gate is read once and loaded nontemporal; the
+// rows keep the default policy, since the line just read is rewritten. Rows past N are handled by range-checked
 // buffer accesses (loads read 0, stores are dropped), so no branch sits between
 // the loads and they all stay in flight together. Mean and variance (two
 // passes over registers, fp32) are reduced with cross-lane exchanges inside a
@@ -28,9 +30,12 @@ namespace {
 
 constexpr int kEpiThreads = 256;
 
+// Cache policy of a load: 0 default, 2 nontemporal.
+template <int POL>
 __device__ inline i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL);
 }
+constexpr int kLoadDefault = 0, kLoadStream = 2;
 __device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, i32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
@@ -67,7 +72,7 @@ struct Piece<bf16_t> {
     }
 };
 
-constexpr int kRowsPerGroup = 64;
+constexpr int kRowsPerGroup = 128;  // 64 and 256 measured slower, 96 and 192 too
 
 // Sum over aligned groups of L adjacent lanes (L = 8, 16 or 32), every lane of
 // a group receiving the total. Within a 16-lane DPP row: exchange with lane^1
@@ -113,8 +118,8 @@ __global__ __launch_bounds__(kEpiThreads) void output_gate_kernel(
     for (int s = 0; s < STEPS; ++s) {
         const int r = (s * WAVES + wave) * RPW + lane / LPR;
         off[s] = static_cast<uint32_t>((r * DV + c0) * sizeof(T));
-        xr[s] = buf_load16(ro, off[s]);
-        gr[s] = buf_load16(rg, off[s]);
+        xr[s] = buf_load16<kLoadDefault>(ro, off[s]);
+        gr[s] = buf_load16<kLoadStream>(rg, off[s]);
     }
     float w[VPL], b[VPL];
 #pragma unroll
