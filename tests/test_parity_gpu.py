@@ -106,6 +106,24 @@ def test_fp32_dims_and_chunks(gret, dk, dv, chunk):
     check_prefill(gret, d, chunk, TOL_F32, S0, label="f32")
 
 
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 128, 129, 191, 256, 257])
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+def test_fp32_short_lengths(gret, N, chunk, dk, dv):
+    # the fp32 kernel stages 64-position sub-chunks: lengths that end inside,
+    # at and just past a sub-chunk or a chunk, with an initial state
+    d, S0 = small_inputs(1, 2, N, dk, dv, dtype="f32", seed=7 * N + chunk + dk)
+    check_prefill(gret, d, chunk, TOL_F32, S0, label="f32 short")
+
+
+@pytest.mark.parametrize("lg_mode", ["one", "zero", "mixed"])
+@pytest.mark.parametrize("chunk", [64, 256])
+def test_fp32_gate_regimes(gret, lg_mode, chunk):
+    # gates = 1 (no decay), gates = 0 (a reset at every position) and mixed
+    d, S0 = small_inputs(2, 2, 300, 128, 128, dtype="f32", seed=31 + chunk, lg_mode=lg_mode)
+    check_prefill(gret, d, chunk, TOL_F32, S0, label="f32 " + lg_mode)
+
+
 # ---------------------------------------------------------------- bf16 path
 
 @pytest.mark.parametrize("chunk", [64, 128, 256])
