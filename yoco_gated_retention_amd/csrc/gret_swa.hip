@@ -241,35 +241,23 @@ __device__ inline void swa_block(const bf16_t* kt, const bf16_t* vt, const bf16x
         }
 }
 
-// Waits until this wavefront's loads of a block have landed while those of
-// `later` (0 .. kSStages - 2) further blocks stay in flight.
-template <int D>
-__device__ inline void wait_blocks(int later) {
-    constexpr int M = SCfg<D>::DMA;
-    if (later >= 2) {
-        wait_vm<2 * M>();
-    } else if (later == 1) {
-        wait_vm<M>();
-    } else {
-        wait_vm<0>();
-    }
-}
-
 // One pipeline step over the block i of n (stage X of kSStages): wait for its
 // loads, refill the stage read one step ago with block i + kSStages - 1,
-// compute.
+// compute. Loads are issued unconditionally so that the compiler's own waits
+// stay out of the loop: with the refill under a branch it made the reads of
+// one stage in every round wait for all loads in flight.
 template <int D, int X>
 __device__ inline void swa_step(int i, int n,
                                 int64_t kb0, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                 const bf16x8 (&qf)[SCfg<D>::KS], int64_t qi, int64_t qw0,
                                 int64_t W, float cl, SwaAcc<D>& st) {
     constexpr int AHEAD = kSStages - 1;
-    const int later = n - 1 - i < AHEAD - 1 ? n - 1 - i : AHEAD - 1;
-    wait_blocks<D>(later);
+    // blocks past the window are loaded too (rows past the head read zeros)
+    // and never used: every step issues the same loads, so the waits are fixed
+    wait_vm<(AHEAD - 1) * SCfg<D>::DMA>();
     lds_barrier();
-    if (i + AHEAD < n)
-        dma_stage<D>(kr, vr, swa_kst<(X + AHEAD) % kSStages>(), swa_vst<(X + AHEAD) % kSStages>(),
-                     static_cast<uint32_t>((kb0 + i + AHEAD) * kSK));
+    dma_stage<D>(kr, vr, swa_kst<(X + AHEAD) % kSStages>(), swa_vst<(X + AHEAD) % kSStages>(),
+                 static_cast<uint32_t>((kb0 + i + AHEAD) * kSK));
     const int64_t key0 = (kb0 + i) * kSK;
     // this wavefront's queries qw0 .. qw0 + 31 see keys qw0 - W + 1 .. qw0 + 31
     const bool active = key0 + kSK > qw0 - W + 1 && key0 <= qw0 + 31;
@@ -323,7 +311,7 @@ __global__ __launch_bounds__(kSThreads) void swa_prefill_kernel(SwaParams p) {
     const float cl = p.scale_log2;
 
     dma_stage<D>(kr, vr, swa_kst<0>(), swa_vst<0>(), static_cast<uint32_t>(kb0 * kSK));
-    if (n > 1) dma_stage<D>(kr, vr, swa_kst<1>(), swa_vst<1>(), static_cast<uint32_t>((kb0 + 1) * kSK));
+    dma_stage<D>(kr, vr, swa_kst<1>(), swa_vst<1>(), static_cast<uint32_t>((kb0 + 1) * kSK));
     if (kSStages > 3 && n > 2)
         dma_stage<D>(kr, vr, swa_kst<2>(), swa_vst<2>(), static_cast<uint32_t>((kb0 + 2) * kSK));
 #define GRET_SWA_STEP(X) swa_step<D, X>(i + X, n, kb0, kr, vr, qf, qi, qw0, W, cl, st)
@@ -338,6 +326,7 @@ __global__ __launch_bounds__(kSThreads) void swa_prefill_kernel(SwaParams p) {
     if (i + 1 < n) GRET_SWA_STEP(1);
     if (kSStages > 3 && i + 2 < n) GRET_SWA_STEP(2);
 #undef GRET_SWA_STEP
+    wait_vm<0>();  // the loads past the window have landed before the LDS is released
 
     if (qi >= N) return;
     const float l = st.l + __shfl_xor(st.l, 32);
