@@ -53,6 +53,8 @@ KERNEL_SOURCES = {
     "decode": ["gret_decode.hip", "gret_internal.h", "gret_device.h"],
     "decode_gated": ["gret_decode.hip", "gret_internal.h", "gret_device.h"],
     "xattn": ["gret_xattn.hip", "gret_internal.h", "gret_device.h"],
+    "prefill_gated": ["gret_prefill_c64.hip", "gret_prefill_common.h", "gret_api.cpp",
+                      "gret_segments.h", "gret_internal.h", "gret_device.h"],
     "epilogue": ["gret_epilogue.hip", "gret_internal.h", "gret_device.h"],
     "proj": ["gret_proj.hip", "gret_internal.h", "gret_device.h"],
     "swa": ["gret_swa.hip", "gret_internal.h", "gret_device.h"],
@@ -117,6 +119,8 @@ def kernel_group(name):
         # the gated instantiation (template flag true; rocprofv3 may leave bf16
         # instantiations mangled, where the flag reads Lb1E)
         return "decode_gated" if ("Lb1E" in name or ", true>" in name) else "decode"
+    if "prefill" in name and ("Lb1E" in name or ", true>" in name):
+        return "prefill_gated"
     if "prefill" in name or "combine" in name:
         return "prefill"
     return "other:" + name.split("(")[0][:60]
@@ -156,10 +160,14 @@ def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir, mfma_dir=None):
     write = pmc_per_dispatch(write_dir, "WRITE_SIZE")
     util = pmc_per_dispatch(mfma_dir, "MfmaUtil") if mfma_dir else {}
     mops = pmc_per_dispatch(mfma_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16") if mfma_dir else {}
-    for which in ("prefill", "decode", "decode_gated", "xattn", "epilogue", "proj", "swa"):
+    for which in ("prefill", "prefill_gated", "decode", "decode_gated", "xattn", "epilogue",
+                  "proj", "swa"):
         names = sorted(k for k in fetch if kernel_group(k) == which)
         if not names:
             continue
+        if which == "prefill_gated":
+            # the combine launch is shared by the plain and the gated prefill
+            names += sorted(k for k in fetch if "combine" in k)
         kern = {}
         for k in names:
             kern[short_kernel_name(k)] = {
@@ -320,11 +328,13 @@ def prefill_roofline(B, H, N, dk, dv, chunk, state_in, ms, kernel, measured_gbs=
 
 def time_prefill_gated(dp, chunk, steps, warmup, dev, seed=3003):
     """Plain and gated prefill on the same resident inputs (gate: seeded normal,
-    bf16; affine: seeded, fp32). The difference of the two call times is the
-    output epilogue's pass."""
+    bf16; affine: seeded, fp32). At chunk 64 the prefill kernels apply the
+    output epilogue in their output store (the gate tile streams into LDS
+    beside the other tiles); at 128 and 256 an in-place pass rewrites the
+    output. The difference of the two call times is the epilogue's cost."""
     import torch
 
-    B, H, N, dv = dp.B, dp.H, dp.N, dp.dv
+    B, H, N, dk, dv = dp.B, dp.H, dp.N, dp.dk, dp.dv
     g = torch.Generator(device=dev).manual_seed(seed)
     gate = (2.0 * torch.randn((B, H, N, dv), generator=g, device=dev)).to(torch.bfloat16)
     w = 1.0 + 0.2 * torch.randn((H, dv), generator=g, device=dev)
@@ -337,17 +347,30 @@ def time_prefill_gated(dp, chunk, steps, warmup, dev, seed=3003):
     del gate, w, b
     torch.cuda.empty_cache()
     rows = B * H * N
-    epi_bytes = rows * dv * 2 * 3 + 2 * H * dv * 4
     epi_ms = gated - plain
+    res = {"workload": "prefill_gated (same inputs) + per-head GroupNorm + swish gate",
+           "ms_per_call": gated, "plain_ms_per_call": plain, "tokens_per_s": B * N / (gated * 1e-3),
+           "timing": "median of %d calls each" % steps, "fused": chunk == 64}
+    if chunk == 64:
+        # the plain prefill's bytes plus the gate rows and the affine
+        nbytes = prefill_algorithmic(B, H, N, dk, dv, chunk, dp.si is not None)[0] + \
+            rows * dv * 2 + 2 * H * dv * 4
+        achieved = nbytes / (gated * 1e-3) / 1e9
+        res["epilogue"] = {"ms": epi_ms, "where": "in the prefill kernels' output store"}
+        res["roofline"] = {"kernel": "prefill_main_c64_kernel<128,128,true> + combine + prefix",
+                           "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                           "algorithmic_bytes_per_launch": nbytes,
+                           "traffic": recorded_traffic("prefill_gated")}
+        return res
+    epi_bytes = rows * dv * 2 * 3 + 2 * H * dv * 4
     achieved = epi_bytes / (epi_ms * 1e-3) / 1e9 if epi_ms > 0 else None
-    return {"workload": "prefill_gated (same inputs) + per-head GroupNorm + swish gate",
-            "ms_per_call": gated, "plain_ms_per_call": plain, "tokens_per_s": B * N / (gated * 1e-3),
-            "timing": "median of %d calls each" % steps,
-            "epilogue": {"ms": epi_ms, "algorithmic_bytes": epi_bytes,
-                         "roofline": {"kernel": "output_gate_kernel (in-place pass)", "bound": "hbm",
-                                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": None if achieved is None else achieved / HBM_PEAK_GBS,
-                                      "traffic": recorded_traffic("epilogue")}}}
+    res["epilogue"] = {"ms": epi_ms, "algorithmic_bytes": epi_bytes,
+                       "roofline": {"kernel": "output_gate_kernel (in-place pass)", "bound": "hbm",
+                                    "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": None if achieved is None else achieved / HBM_PEAK_GBS,
+                                    "traffic": recorded_traffic("epilogue")}}
+    return res
 
 
 STREAM_LIB = os.path.join(ROOT, "yoco_gated_retention_amd", "libgret_stream.so")

@@ -207,8 +207,12 @@ int gret_decode_step(const void* q, const void* k, const void* v, const float* l
  *                0 by 0
  * out must not overlap gate, norm_weight or norm_bias (GRET_ERR_ALIAS); every
  * other argument and rule is that of the plain entry point. The statistics are
- * computed in fp32 from the fp32 retention output in the decode step, and from
- * the stored output (dtype) in prefill, which then rewrites out in place.
+ * computed in fp32: from the fp32 retention output in the decode step, and in
+ * prefill from the output rounded to dtype (what the plain entry point would
+ * store). In the bf16 prefill with chunk 64 the prefill kernels apply the
+ * epilogue in their output store; with chunk 128 or 256, and in fp32, the
+ * plain output is stored and a second pass rewrites out in place. Both give
+ * the same values.
  */
 int gret_prefill_gated(const void* q, const void* k, const void* v, const float* log_gamma,
                        const float* state_in, const void* gate, const float* norm_weight,

@@ -137,6 +137,34 @@ def test_prefill_gated_32k_all_heads(gret):
     check_prefill_gated(gret, d, None, gate, w, b, 1e-5, 64, TOL_BF16, "32k")
 
 
+@pytest.mark.timeout(900)
+def test_prefill_gated_512k_sampled_heads(gret):
+    """The 512K workload through the gated prefill (all 24 heads, the launch
+    configuration the benchmark times); heads 0, 11 and 23 against the oracle
+    chain. Every head spans about eleven segments, so the output-free leading
+    chunks and their recomputation from the incoming state are covered."""
+    d = make_prefill_inputs("prefill_512k")
+    B, H, N, dv = d["q"].shape[0], d["q"].shape[1], d["q"].shape[2], d["v"].shape[3]
+    rng = np.random.default_rng(3003)
+    gate = f32_to_bf16_bits(rng.standard_normal((B, H, N, dv), dtype=np.float32) * np.float32(2.0))
+    w = (1.0 + 0.2 * rng.standard_normal((H, dv))).astype(np.float32)
+    b = (0.2 * rng.standard_normal((H, dv))).astype(np.float32)
+    say("prefill_gated 512K, all heads on the GPU")
+    out, st = gret.gret_prefill_gated(
+        to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"]), to_dev(d["log_gamma"]), to_dev(gate),
+        norm_weight=to_dev(w), norm_bias=to_dev(b), norm_eps=1e-5, chunk=64)
+    torch.cuda.synchronize()
+    y, st = to_host(out), to_host(st)
+    for h in (0, 11, 23):
+        sl = lambda a: np.ascontiguousarray(a[:, h:h + 1])
+        o_ref, s_ref, _ = oracle.oracle_prefill_f64(sl(d["q"]), sl(d["k"]), sl(d["v"]),
+                                                    sl(d["log_gamma"]), None)
+        y_ref = oracle_output_gate_f64(o_ref, sl(gate), w[h:h + 1], b[h:h + 1], eps=1e-5)
+        e_y, e_s = eps(y[:, h:h + 1], y_ref), eps(st[:, h:h + 1], s_ref)
+        say("   head %d: eps_y=%.3e eps_state=%.3e" % (h, e_y, e_s))
+        assert e_y <= TOL_BF16 and e_s <= TOL_BF16, (h, e_y, e_s)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
 def test_decode_gated_small(gret, dtype, dk, dv):

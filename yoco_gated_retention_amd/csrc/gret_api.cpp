@@ -244,8 +244,12 @@ int prefill_impl(const void* q, const void* k, const void* v, const float* log_g
         a.workspace_bytes = GRET_NOALLOC_SCRATCH_BYTES;
         if (!a.workspace) return GRET_ERR_HIP;
     }
+    // chunk 64: the kernels apply the epilogue in their output store; the
+    // other chunk sizes store the plain output and a pass rewrites it
+    const bool fused = epi && chunk == 64;
+    if (fused) a.epi = *epi;
     st = hip_status(gret::launch_prefill_bf16(a, plan));
-    if (st != GRET_OK || !epi) return st;
+    if (st != GRET_OK || !epi || fused) return st;
     return hip_status(gret::launch_output_gate_bf16(ea));
 }
 

@@ -32,9 +32,6 @@ namespace {
 
 constexpr int kDecodeThreads = 256;
 
-// swish(x) = x * sigmoid(x), with the hardware reciprocal (about 1 ulp).
-__device__ inline float swish(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
-
 template <typename T, int DK, int DV, bool GATED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,

@@ -67,6 +67,26 @@ __device__ inline bf16x8 cat44(const bf16x4& a, const bf16x4& b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// swish(x) = x * sigmoid(x), with the hardware reciprocal (about 1 ulp).
+__device__ inline float swish(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
+// Sum over aligned groups of L adjacent lanes (L = 8, 16 or 32), every lane of
+// a group receiving the total. Within a 16-lane DPP row: exchange with lane^1
+// and lane^2 (quad permutations), then with the mirrored lane of the half row
+// and of the row; across rows (L = 32) one cross-lane permute.
+template <int L>
+__device__ inline float group_sum(float v) {
+    static_assert(L == 8 || L == 16 || L == 32, "group size");
+    constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kXor1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kXor2, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kHalfMirror, 0xF, 0xF, false));
+    if constexpr (L >= 16)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kMirror, 0xF, 0xF, false));
+    if constexpr (L == 32) v += __shfl_xor(v, 16);
+    return v;
+}
+
 // Range-checked buffer access (CDNA buffer resources): a load past the
 // descriptor's byte size returns zeros and a store past it is dropped.
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, gfx9-family data format

@@ -1,5 +1,7 @@
 // gret_epilogue.hip -- output epilogue of gated retention on gfx950, applied in
-// place to a stored retention output.
+// place to a stored retention output (the fp32 prefill and the bf16 prefill at
+// chunk 128 and 256; at chunk 64 the prefill kernels apply it in their output
+// store).
 //
 // Page "YOCO 完全拆解：Decoder-Decoder 架构如何让 KV Cache 只存一次", section
 // "路线二：Multi-Head Gated Retention": the multi-head output is normalised per
@@ -40,9 +42,6 @@ __device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, i32x4
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
 
-// swish(x) = x * sigmoid(x), with the hardware reciprocal (about 1 ulp).
-__device__ inline float swish(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
-
 template <typename T>
 struct Piece;  // one 16-byte piece of a row, widened to fp32
 template <>
@@ -73,23 +72,6 @@ struct Piece<bf16_t> {
 };
 
 constexpr int kRowsPerGroup = 128;  // 64 and 256 measured slower, 96 and 192 too
-
-// Sum over aligned groups of L adjacent lanes (L = 8, 16 or 32), every lane of
-// a group receiving the total. Within a 16-lane DPP row: exchange with lane^1
-// and lane^2 (quad permutations), then with the mirrored lane of the half row
-// and of the row; across rows (L = 32) one cross-lane permute.
-template <int L>
-__device__ inline float group_sum(float v) {
-    static_assert(L == 8 || L == 16 || L == 32, "group size");
-    constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kXor1, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kXor2, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kHalfMirror, 0xF, 0xF, false));
-    if constexpr (L >= 16)
-        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kMirror, 0xF, 0xF, false));
-    if constexpr (L == 32) v += __shfl_xor(v, 16);
-    return v;
-}
 
 template <typename T, int DV>
 __global__ __launch_bounds__(kEpiThreads) void output_gate_kernel(

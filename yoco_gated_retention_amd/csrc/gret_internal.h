@@ -25,6 +25,14 @@ constexpr float kSurvivalDropLog = -20.0f;
 // every launch of a call against it before anything is enqueued.
 constexpr int64_t kMaxGridGroups = 0x7fffffff;
 
+// Output epilogue (per-head GroupNorm + swish gate); gate == nullptr means none.
+struct OutputGate {
+    const void* gate = nullptr;
+    const float* weight = nullptr;  // [H][dv] or null
+    const float* bias = nullptr;    // [H][dv] or null
+    float eps = 0.0f;
+};
+
 struct PrefillArgs {
     const void* q;
     const void* k;
@@ -37,14 +45,7 @@ struct PrefillArgs {
     void* workspace;
     size_t workspace_bytes;
     hipStream_t stream;
-};
-
-// Output epilogue (per-head GroupNorm + swish gate); gate == nullptr means none.
-struct OutputGate {
-    const void* gate = nullptr;
-    const float* weight = nullptr;  // [H][dv] or null
-    const float* bias = nullptr;    // [H][dv] or null
-    float eps = 0.0f;
+    OutputGate epi;  // applied by the chunk-64 bf16 kernels in their output store
 };
 
 struct DecodeArgs {

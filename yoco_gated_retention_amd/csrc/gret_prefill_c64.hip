@@ -38,7 +38,16 @@
 //              which only it reads) and leaves with full-row 16-byte stores
 //              one chunk later;
 //   * state    S = exp(g) S + K^T (Gamma V), Gamma_l = exp(g - beta_l).
+//
+// Gated kernels (template flag): the output epilogue of the same page and
+// section (per-head GroupNorm, then the swish output gate) is applied as each
+// output tile leaves LDS. The gate tile streams into an LDS buffer of its own,
+// one chunk ahead; the queries are double-buffered to make room for it. The
+// output rows are normalised from the bf16 tile, the values the plain kernel
+// stores, so the result equals the plain prefill followed by the epilogue pass.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "gret_prefill_common.h"
 
@@ -102,26 +111,47 @@ __device__ inline int toff_t(int row, int col) {
     return row * D + (((col >> 3) ^ tswz<D, T>(row)) << 3) + (col & 7);
 }
 
+// A per-lane LDS offset that the compiler may neither move out of the chunk
+// loop nor merge with another:
+//  * hoisted, base + offset is one register per buffer of a kind and per
+//    offset for the whole loop (three copies of every Q, K and V operand
+//    address); kept in the loop, the buffer's base folds into the
+//    instruction's offset field and one register per offset serves every
+//    buffer. That frees the registers that the gated kernels' epilogue needs
+//    (without it they spill 71 registers);
+//  * two 8-byte accesses a constant distance apart would otherwise become one
+//    ds_read2st64_b64 / ds_write2st64_b64, which measured at a third of the
+//    throughput of the two separate accesses.
+__device__ inline int pinned(int off) {
+    asm volatile("" : "+v"(off));
+    return off;
+}
+
+// The plain kernels keep the hoisted addresses (they fit, and measured about
+// 1 % faster) and only block the merging of 8-byte accesses (sep).
+template <bool PIN>
+__device__ inline int loff(int off) {
+    if constexpr (PIN) return pinned(off);
+    return off;
+}
+template <bool PIN>
+__device__ inline int sep(int off) {
+    if constexpr (PIN) return pinned(off);
+    asm("" : "+v"(off));
+    return off;
+}
+
 // 8 consecutive positions t0..t0+7 of column col0 + l (l = this lane's index
 // in its 16-lane group) of a tile: the MFMA operand for a contraction over
 // positions, read with the transposing LDS load.
-template <int D, int T>
+template <int D, int T, bool PIN>
 __device__ inline bf16x8 read_cols8_t(const bf16_t* tile, int t0, int col0) {
     const int s = threadIdx.x & 15;
     const int row = t0 + (s >> 2);
     const int col = col0 + 4 * (s & 3);
-    const bf16x4 a = lds_read_tr4(tile + toff_t<D, T>(row, col));
-    const bf16x4 b = lds_read_tr4(tile + toff_t<D, T>(row + 4, col));
+    const bf16x4 a = lds_read_tr4(tile + loff<PIN>(toff_t<D, T>(row, col)));
+    const bf16x4 b = lds_read_tr4(tile + loff<PIN>(toff_t<D, T>(row + 4, col)));
     return cat44(a, b);
-}
-
-// Hides an LDS offset from the compiler's load/store merging: two 8-byte
-// accesses a constant distance apart would otherwise become one
-// ds_read2st64_b64 / ds_write2st64_b64, which measured at a third of the
-// throughput of the two separate accesses.
-__device__ inline int opaque(int off) {
-    asm("" : "+v"(off));
-    return off;
 }
 
 // First value column of column tile ct of this wavefront.
@@ -194,7 +224,7 @@ struct TileView {
 // dk = 32m + {4g..4g+3, 16+4g..16+4g+3}; the Q operand is read with the same
 // permutation of dk, so the contraction pairs matching indices. Each Q
 // fragment serves all column tiles of the wavefront.
-template <int DK, int DV>
+template <int DK, int DV, bool PIN>
 __device__ inline void cross_term(const TileView& tv, const Acc<DK, DV>& a,
                                   f32x4 (&o)[C64<DK, DV>::CT][4]) {
     using c = C64<DK, DV>;
@@ -217,8 +247,8 @@ __device__ inline void cross_term(const TileView& tv, const Acc<DK, DV>& a,
         for (int jt = 0; jt < 4; ++jt) {
             const int row = 16 * jt + li;
             const bf16x8 qf =
-                cat44(lds_read4(tv.qs + opaque(toff_t<DK, kTileQ>(row, 32 * m + 4 * g))),
-                      lds_read4(tv.qs + opaque(toff_t<DK, kTileQ>(row, 32 * m + 16 + 4 * g))));
+                cat44(lds_read4(tv.qs + sep<PIN>(toff_t<DK, kTileQ>(row, 32 * m + 4 * g))),
+                      lds_read4(tv.qs + sep<PIN>(toff_t<DK, kTileQ>(row, 32 * m + 16 + 4 * g))));
 #pragma unroll
             for (int ct = 0; ct < c::CT; ++ct) o[ct][jt] = mfma16(sf[ct], qf, o[ct][jt]);
         }
@@ -238,7 +268,7 @@ __device__ inline void cross_term(const TileView& tv, const Acc<DK, DV>& a,
 
 // Decayed score block (jb, b): query rows 16jb.. against key positions 16b..,
 // written as bf16 to ps[j][l]; entries above the diagonal are zero.
-template <int DK, int DV>
+template <int DK, int DV, bool PIN>
 __device__ inline void score_block(const TileView& tv, bf16_t* ps, int jb, int b) {
     using c = C64<DK, DV>;
     const int lane = threadIdx.x & 63;
@@ -248,8 +278,8 @@ __device__ inline void score_block(const TileView& tv, bf16_t* ps, int jb, int b
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < c::KS; ++ks) {
-        const bf16x8 qf = lds_read8(tv.qs + toff_t<DK, kTileQ>(jrow, 32 * ks + 8 * g));
-        const bf16x8 kf = lds_read8(tv.ks + toff_t<DK, kTileK>(16 * b + li, 32 * ks + 8 * g));
+        const bf16x8 qf = lds_read8(tv.qs + loff<PIN>(toff_t<DK, kTileQ>(jrow, 32 * ks + 8 * g)));
+        const bf16x8 kf = lds_read8(tv.ks + loff<PIN>(toff_t<DK, kTileK>(16 * b + li, 32 * ks + 8 * g)));
         acc = mfma16(kf, qf, acc);
     }
     // acc[i] = P^T[l = 16b + 4g + i][j = jrow]
@@ -264,12 +294,12 @@ __device__ inline void score_block(const TileView& tv, bf16_t* ps, int jb, int b
 }
 
 // Wavefront w computes causal blocks w, w + NW, ...
-template <int DK, int DV>
+template <int DK, int DV, bool PIN>
 __device__ inline void scores_diag(const TileView& tv, bf16_t* ps) {
     const int w = threadIdx.x >> 6;
     for (int i = w; i < 10; i += C64<DK, DV>::NW) {
         const int e = static_cast<int>((kCausalBlocks >> (4 * i)) & 0xF);
-        score_block<DK, DV>(tv, ps, e >> 2, e & 3);
+        score_block<DK, DV, PIN>(tv, ps, e >> 2, e & 3);
     }
 }
 
@@ -288,7 +318,7 @@ __device__ inline void zero_upper_blocks(bf16_t* ps) {
 
 // O^T[cols][rows] += V^T P~^T (V read transposed); 32-position steps wholly
 // above the diagonal are skipped. Each P~ fragment serves all column tiles.
-template <int DK, int DV>
+template <int DK, int DV, bool PIN>
 __device__ inline void apply_scores(const bf16_t* ps, const bf16_t* vs,
                                     f32x4 (&o)[C64<DK, DV>::CT][4]) {
     using c = C64<DK, DV>;
@@ -298,7 +328,7 @@ __device__ inline void apply_scores(const bf16_t* ps, const bf16_t* vs,
     for (int ks = 0; ks < 2; ++ks) {
         bf16x8 vf[c::CT];
 #pragma unroll
-        for (int ct = 0; ct < c::CT; ++ct) vf[ct] = read_cols8_t<DV, kTileV>(vs, 32 * ks + 8 * g, col0<DK, DV>(ct));
+        for (int ct = 0; ct < c::CT; ++ct) vf[ct] = read_cols8_t<DV, kTileV, PIN>(vs, 32 * ks + 8 * g, col0<DK, DV>(ct));
 #pragma unroll
         for (int jt = 2 * ks; jt < 4; ++jt) {
             const bf16x8 pf = lds_read8(ps + (16 * jt + li) * c::PP + 32 * ks + 8 * g);
@@ -311,7 +341,7 @@ __device__ inline void apply_scores(const bf16_t* ps, const bf16_t* vs,
 // S += K^T (Gamma V) over the chunk; K and V are read transposed so that
 // positions are the contraction index. Each K fragment serves all column
 // tiles.
-template <int DK, int DV>
+template <int DK, int DV, bool PIN>
 __device__ inline void state_update(const TileView& tv, Acc<DK, DV>& a) {
     using c = C64<DK, DV>;
     const int lane = threadIdx.x & 63;
@@ -324,7 +354,7 @@ __device__ inline void state_update(const TileView& tv, Acc<DK, DV>& a) {
         bf16x8 bf[c::CT];
 #pragma unroll
         for (int ct = 0; ct < c::CT; ++ct) {
-            const bf16x8 vf = read_cols8_t<DV, kTileV>(tv.vs, t0, col0<DK, DV>(ct));
+            const bf16x8 vf = read_cols8_t<DV, kTileV, PIN>(tv.vs, t0, col0<DK, DV>(ct));
             bf[ct] = bf16x8{to_bf16(from_bf16(vf[0]) * g0[0]), to_bf16(from_bf16(vf[1]) * g0[1]),
                             to_bf16(from_bf16(vf[2]) * g0[2]), to_bf16(from_bf16(vf[3]) * g0[3]),
                             to_bf16(from_bf16(vf[4]) * g1[0]), to_bf16(from_bf16(vf[5]) * g1[1]),
@@ -332,7 +362,7 @@ __device__ inline void state_update(const TileView& tv, Acc<DK, DV>& a) {
         }
 #pragma unroll
         for (int tk = 0; tk < c::TK; ++tk) {
-            const bf16x8 kf = read_cols8_t<DK, kTileK>(tv.ks, t0, 16 * tk);
+            const bf16x8 kf = read_cols8_t<DK, kTileK, PIN>(tv.ks, t0, 16 * tk);
 #pragma unroll
             for (int ct = 0; ct < c::CT; ++ct) a.s[ct][tk] = mfma16(kf, bf[ct], a.s[ct][tk]);
         }
@@ -341,7 +371,7 @@ __device__ inline void state_update(const TileView& tv, Acc<DK, DV>& a) {
 
 // The chunk's output into its own V buffer (swizzled row-major, bf16): each
 // lane's fragment is 4 consecutive columns of one row.
-template <int DK, int DV>
+template <int DK, int DV, bool PIN>
 __device__ inline void out_to_lds(bf16_t* vs, const f32x4 (&o)[C64<DK, DV>::CT][4]) {
     using c = C64<DK, DV>;
     const int lane = threadIdx.x & 63;
@@ -353,7 +383,7 @@ __device__ inline void out_to_lds(bf16_t* vs, const f32x4 (&o)[C64<DK, DV>::CT][
             const bf16x4 pk = {to_bf16(o[ct][jt][0]), to_bf16(o[ct][jt][1]),
                                to_bf16(o[ct][jt][2]), to_bf16(o[ct][jt][3])};
             *reinterpret_cast<bf16x4*>(
-                vs + opaque(toff_t<DV, kTileV>(16 * jt + li, col0<DK, DV>(ct) + 4 * g))) = pk;
+                vs + sep<PIN>(toff_t<DV, kTileV>(16 * jt + li, col0<DK, DV>(ct) + 4 * g))) = pk;
         }
 }
 
@@ -435,6 +465,8 @@ struct Lds {
     float* tab[3];  // beta[64] | gam[64] | fexp[64]
     bf16_t* ps;
     float* sink;    // target of the log-gate DMA of wavefronts other than 0
+    bf16_t* gt;     // gated kernels: gate tile of the output being flushed
+    float* aff;     // gated kernels: the head's norm weight[DV] | bias[DV]
 };
 
 // Issues this wavefront's share of the DMA of the tile at tile_pos into set X.
@@ -495,6 +527,70 @@ __device__ inline void flush_tile(const bf16_t* vs, const __amdgpu_buffer_rsrc_t
     for (int i = 0; i < c::VB; ++i) flush_block<DV, kTileV>(out, vs, w * c::VB + i, tile_pos);
 }
 
+// The gate rows of the tile at tile_pos into the gate buffer, in the layout of
+// a V tile: each wavefront loads the blocks whose outputs it flushes.
+template <int DK, int DV>
+__device__ inline void dma_gate(bf16_t* gt, const __amdgpu_buffer_rsrc_t& g, uint32_t tile_pos) {
+    using c = C64<DK, DV>;
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < c::VB; ++i) dma_block<DV, kTileV>(g, gt, w * c::VB + i, tile_pos);
+}
+
+// flush_tile with the output epilogue of gated retention (page "YOCO 完全拆解：
+// Decoder-Decoder 架构如何让 KV Cache 只存一次", section "路线二：Multi-Head Gated
+// Retention": per-head GroupNorm over the dv channels of a position, then the
+// element-wise gate swish(X W_G)). Lane i holds 8 channels of one row, a row's
+// DV / 8 lanes are adjacent, so mean and variance (two passes, fp32) are
+// reductions inside a lane group; the gate piece sits at the same LDS offset
+// in the gate buffer, the affine of the piece's channels in aff.
+//   y = swish(gate) * ((o - mean) / sqrt(var + eps) * w + b)
+template <int DK, int DV>
+__device__ inline void flush_tile_gated(const bf16_t* vs, const bf16_t* gt, const float* aff,
+                                        const __amdgpu_buffer_rsrc_t& out, uint32_t tile_pos,
+                                        float eps) {
+    using c = C64<DK, DV>;
+    constexpr int RPI = 512 / DV;
+    constexpr int SPR = DV / 8;
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < c::VB; ++i) {
+        const int blk = w * c::VB + i;
+        const int row = RPI * blk + lane / SPR;
+        const int chunk = (lane % SPR) ^ tswz<DV, kTileV>(row);
+        const int po = pinned(blk * 512 + 8 * lane);
+        const bf16x8 xv = lds_read8(vs + po);
+        const bf16x8 gv = lds_read8(gt + po);
+        const int a0 = pinned(chunk * 8);
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(aff + a0);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(aff + a0 + 4);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(aff + DV + a0);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(aff + DV + a0 + 4);
+        float x[8];
+        float sum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            x[e] = from_bf16(xv[e]);
+            sum += x[e];
+        }
+        const float mean = group_sum<SPR>(sum) * (1.0f / DV);
+        float sq = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sq += (x[e] - mean) * (x[e] - mean);
+        const float rstd = rsqrtf(group_sum<SPR>(sq) * (1.0f / DV) + eps);
+        bf16x8 y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float we = e < 4 ? w0[e] : w1[e - 4];
+            const float be = e < 4 ? b0[e] : b1[e - 4];
+            y[e] = to_bf16(swish(from_bf16(gv[e])) * ((x[e] - mean) * rstd * we + be));
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, y), out,
+                                               ((tile_pos + row) * DV + chunk * 8) * 2, 0, 0);
+    }
+}
+
 // Waits until this wavefront's DMA writes of the tile used by the k-th chunk of
 // the pass are complete. Chunk j issues the stores of chunk j-1's output, then
 // the DMA of tile j+2, so the operations younger than tile k's DMA (issued by
@@ -509,10 +605,10 @@ __device__ inline void wait_tile(int k) {
         wait_vm<c::DMA + c::ST>();
 }
 
-// One chunk of the pipeline, buffer set X. prev_out is where the previous
-// chunk's output goes (the head's output, or a zero-size range that drops it
-// while a segment only advances its state); it is flushed from V buffer
-// (X + 2) % 3 just before the DMA of tile k + 2 reuses that set.
+// One chunk of the pipeline, buffer set X, query buffer QX. prev_out is where
+// the previous chunk's output goes (the head's output, or a zero-size range
+// that drops it while a segment only advances its state); it is flushed from V
+// buffer (X + 2) % 3 just before the DMA of tile k + 2 reuses that set.
 //
 // `full` says whether this chunk's outputs are computed (its queries were
 // loaded); otherwise the chunk only advances the state. The running log-decay
@@ -520,16 +616,30 @@ __device__ inline void wait_tile(int k) {
 // `next_full` receives the mode of tile k + 2, whose DMA this chunk issues:
 // full when the caller asked for every output, or once the running log-decay
 // through this chunk is below kSurvivalDropLog.
-template <int DK, int DV, int X>
+//
+// GATED: the flush applies the output epilogue, with the gate rows of the
+// flushed tile in the gate buffer (loaded one chunk earlier, right after that
+// chunk's flush). The queries are double-buffered (QX = k % 2) to make room
+// for it, so the DMA of tile k + 2's queries waits until every wavefront is
+// done with tile k's scores. Per chunk each wavefront then issues: ST stores,
+// VB gate loads, then QB keys, QB queries, VB values and 1 log-gate load for
+// tile k + 2; the wait at the chunk start leaves only the last DMA of those
+// outstanding, so the gate of tile k - 1 and all of tile k have landed.
+template <int DK, int DV, int X, int QX, bool GATED>
 __device__ inline void chunk(const Lds<DK, DV>& L, const HeadRsrc& hr,
+                             const __amdgpu_buffer_rsrc_t& gate_r,
                              const __amdgpu_buffer_rsrc_t& prev_out,
                              const __amdgpu_buffer_rsrc_t& no_q, int k, uint32_t pos, bool full,
-                             bool all_full, float& total, bool& next_full, Acc<DK, DV>& a) {
+                             bool all_full, float eps, float& total, bool& next_full,
+                             Acc<DK, DV>& a) {
     using c = C64<DK, DV>;
-    wait_tile<DK, DV>(k);
+    if constexpr (GATED)
+        wait_vm<c::DMA>();
+    else
+        wait_tile<DK, DV>(k);
     if (threadIdx.x < 64) tables_from_lds(L.ell[X], L.tab[X]);
     lds_barrier();
-    const TileView tv{L.q[X], L.k[X], L.v[X], L.tab[X], L.tab[X] + 64, L.tab[X] + 128};
+    const TileView tv{L.q[QX], L.k[X], L.v[X], L.tab[X], L.tab[X] + 64, L.tab[X] + 128};
     const float gc = tv.beta[kTile - 1];
     total += gc;
     next_full = all_full || total < kSurvivalDropLog;
@@ -538,20 +648,43 @@ __device__ inline void chunk(const Lds<DK, DV>& L, const HeadRsrc& hr,
     // the eight wavefronts' memory instructions do not queue up behind each
     // other at the start of the chunk.
     constexpr int Y = (X + 2) % 3;
-    if (k > 0) flush_tile<DK, DV>(L.v[Y], prev_out, pos - kTile);
-    dma_q<DK, DV, Y>(L, next_full ? hr.q : no_q, pos + 2 * kTile);
+    if constexpr (GATED) {
+        flush_tile_gated<DK, DV>(L.v[Y], L.gt, L.aff, prev_out, pos - kTile, eps);
+        dma_gate<DK, DV>(L.gt, full ? gate_r : no_q, pos);
+    } else {
+        if (k > 0) flush_tile<DK, DV>(L.v[Y], prev_out, pos - kTile);
+        dma_q<DK, DV, Y>(L, next_full ? hr.q : no_q, pos + 2 * kTile);
+    }
     f32x4 o[c::CT][4];
-    if (full) cross_term<DK, DV>(tv, a, o);
+    if (full) cross_term<DK, DV, GATED>(tv, a, o);
     dma_k<DK, DV, Y>(L, hr, pos + 2 * kTile);
-    if (full) scores_diag<DK, DV>(tv, L.ps);
-    dma_v_ell<DK, DV, Y>(L, hr, no_q, pos + 2 * kTile);
-    if (full) {
-        lds_barrier();
-        apply_scores<DK, DV>(L.ps, tv.vs, o);
+    if (full) scores_diag<DK, DV, GATED>(tv, L.ps);
+    if constexpr (GATED) {
+        if (full) lds_barrier();
+        dma_q<DK, DV, QX>(L, next_full ? hr.q : no_q, pos + 2 * kTile);
+        dma_v_ell<DK, DV, Y>(L, hr, no_q, pos + 2 * kTile);
+        if (full) apply_scores<DK, DV, GATED>(L.ps, tv.vs, o);
+    } else {
+        dma_v_ell<DK, DV, Y>(L, hr, no_q, pos + 2 * kTile);
+        if (full) {
+            lds_barrier();
+            apply_scores<DK, DV, GATED>(L.ps, tv.vs, o);
+        }
     }
     scale_state<DK, DV>(a, __expf(gc));
-    state_update<DK, DV>(tv, a);
-    if (full) out_to_lds<DK, DV>(L.v[X], o);
+    state_update<DK, DV, GATED>(tv, a);
+    if (full) out_to_lds<DK, DV, GATED>(L.v[X], o);
+}
+
+// Calls f(integral_constant<int, J>) for J = I .. P-1 while it returns true.
+template <int I, int P, class F>
+__device__ inline bool unrolled_steps(F& f) {
+    if constexpr (I == P) {
+        return true;
+    } else {
+        if (!f(std::integral_constant<int, I>{})) return false;
+        return unrolled_steps<I + 1, P>(f);
+    }
 }
 
 // Runs chunks [cb, ce) of head x. With full_from_start the pass computes and
@@ -561,17 +694,19 @@ __device__ inline void chunk(const Lds<DK, DV>& L, const HeadRsrc& hr,
 // chunks ahead; earlier chunks load no queries and only advance the state).
 // Returns the total log-decay; *lead receives the number of output-free
 // chunks. Reads past the head's end return zeros, so the loop has no tail
-// case; the loop is unrolled by three so that every access's buffer set is a
+// case; the loop is unrolled by the period of the buffer indices (three sets,
+// times two query buffers when GATED) so that every access's buffer is a
 // compile-time fact.
 // ALL_FULL compiles the pass that computes every output (the prefix launch)
 // without the mode bookkeeping.
-template <int DK, int DV, bool ALL_FULL = false>
+template <int DK, int DV, bool GATED, bool ALL_FULL = false>
 __device__ float run_chunks(const Params& p, const Lds<DK, DV>& L, int64_t x, int64_t cb,
                            int64_t ce, bool full_from_start, Acc<DK, DV>& a, int64_t* lead) {
     float total = 0.0f;
     const HeadRsrc hr = head_rsrc<DK, DV>(p, x);
     // a zero-size range: stores through it are dropped, loads move no data
     const __amdgpu_buffer_rsrc_t drop = make_rsrc(p.out, 0);
+    __amdgpu_buffer_rsrc_t gate_r = drop;
     const int nch = static_cast<int>(ce - cb);
     const bool all = ALL_FULL || full_from_start;
     uint32_t pos = static_cast<uint32_t>(cb * kTile);
@@ -579,44 +714,56 @@ __device__ float run_chunks(const Params& p, const Lds<DK, DV>& L, int64_t x, in
     // every wavefront finish reading the buffers
     wait_vm<0>();
     lds_barrier();
+    if constexpr (GATED) {
+        gate_r = make_rsrc(p.gate + x * p.N * DV, static_cast<uint32_t>(p.N * DV * 2));
+        // the head's norm affine, read by every flush of the pass (after the
+        // barrier of the first chunk)
+        const int64_t h = x % p.H;
+        for (int e = threadIdx.x; e < 2 * DV; e += C64<DK, DV>::NT)
+            L.aff[e] = e < DV ? (p.gate_w ? p.gate_w[h * DV + e] : 1.0f)
+                              : (p.gate_b ? p.gate_b[h * DV + e - DV] : 0.0f);
+    }
     // modes of the tiles in buffer sets 0, 1, 2
-    bool f0 = all, f1 = all, f2 = all;
+    bool f[3] = {all, all, all};
     dma_tile<DK, DV, 0>(L, hr, all ? hr.q : drop, drop, pos);
     dma_tile<DK, DV, 1>(L, hr, all ? hr.q : drop, drop, pos + kTile);
     int first_full = all ? 0 : nch;  // first chunk whose outputs are written
-    auto note = [&](bool f, int k) {
-        if (f && first_full > k) first_full = k;
-    };
     __amdgpu_buffer_rsrc_t prev = drop;  // destination of the staged output
     int last = 0;                        // buffer set holding it
-    for (int k = 0;; k += 3, pos += 3 * kTile) {
-        if (k >= nch) break;
-        note(f0, k);
-        chunk<DK, DV, 0>(L, hr, prev, drop, k, pos, f0, all, total, f2, a);
-        prev = f0 ? hr.out : drop;
-        last = 0;
-        if (k + 1 >= nch) break;
-        note(f1, k + 1);
-        chunk<DK, DV, 1>(L, hr, prev, drop, k + 1, pos + kTile, f1, all, total, f0, a);
-        prev = f1 ? hr.out : drop;
-        last = 1;
-        if (k + 2 >= nch) break;
-        note(f2, k + 2);
-        chunk<DK, DV, 2>(L, hr, prev, drop, k + 2, pos + 2 * kTile, f2, all, total, f1, a);
-        prev = f2 ? hr.out : drop;
-        last = 2;
-    }
+    int k = 0;
+    auto step = [&](auto J) -> bool {
+        constexpr int j = decltype(J)::value;
+        constexpr int X = j % 3;
+        constexpr int QX = GATED ? j % 2 : X;
+        if (k + j >= nch) return false;
+        if (f[X] && first_full > k + j) first_full = k + j;
+        chunk<DK, DV, X, QX, GATED>(L, hr, gate_r, prev, drop, k + j, pos + j * kTile, f[X], all,
+                                    p.eps, total, f[(X + 2) % 3], a);
+        prev = f[X] ? hr.out : drop;
+        last = X;
+        return true;
+    };
+    constexpr int kPeriod = GATED ? 6 : 3;
+    for (;; k += kPeriod, pos += kPeriod * kTile)
+        if (!unrolled_steps<0, kPeriod>(step)) break;
     *lead = first_full;
     // the last chunk's output: every wavefront's columns must be staged first
+    // (and, GATED, this wavefront's gate rows must have landed)
+    if constexpr (GATED) wait_vm<0>();
     lds_barrier();
     const uint32_t last_pos = static_cast<uint32_t>((ce - 1) * kTile);
-    flush_tile<DK, DV>(last == 0 ? L.v[0] : last == 1 ? L.v[1] : L.v[2], prev, last_pos);
+    const bf16_t* last_v = last == 0 ? L.v[0] : last == 1 ? L.v[1] : L.v[2];
+    if constexpr (GATED)
+        flush_tile_gated<DK, DV>(last_v, L.gt, L.aff, prev, last_pos, p.eps);
+    else
+        flush_tile<DK, DV>(last_v, prev, last_pos);
     wait_vm<0>();  // no DMA into this workgroup's LDS may outlive the pass
     return total;
 }
 
 // LDS of the kernels: three buffer sets, each array its own object (the
-// compiler orders LDS reads after pending LDS DMA per object).
+// compiler orders LDS reads after pending LDS DMA per object). The gated
+// kernels have two query buffers, the gate buffer and the norm affine.
 #define GRET_C64_LDS(DK, DV)                                                              \
     __shared__ __attribute__((aligned(16))) bf16_t q0_[kTile * DK], q1_[kTile * DK],      \
         q2_[kTile * DK];                                                                  \
@@ -630,11 +777,26 @@ __device__ float run_chunks(const Params& p, const Lds<DK, DV>& L, int64_t x, in
     __shared__ __attribute__((aligned(16))) bf16_t ps_[kTile * C64<DK, DV>::PP];          \
     __shared__ __attribute__((aligned(16))) float sink_[kTile];                           \
     const Lds<DK, DV> L{{q0_, q1_, q2_}, {k0_, k1_, k2_}, {v0_, v1_, v2_},                \
-                        {l0_, l1_, l2_}, {t0_, t1_, t2_}, ps_, sink_};
+                        {l0_, l1_, l2_}, {t0_, t1_, t2_}, ps_, sink_, nullptr, nullptr};
 
-template <int DK, int DV>
-__global__ __launch_bounds__(kThreadsFor<DV>) void prefill_main_c64_kernel(Params p) {
-    GRET_C64_LDS(DK, DV)
+#define GRET_C64_LDS_GATED(DK, DV)                                                        \
+    __shared__ __attribute__((aligned(16))) bf16_t q0_[kTile * DK], q1_[kTile * DK];      \
+    __shared__ __attribute__((aligned(16))) bf16_t k0_[kTile * DK], k1_[kTile * DK],      \
+        k2_[kTile * DK];                                                                  \
+    __shared__ __attribute__((aligned(16))) bf16_t v0_[kTile * DV], v1_[kTile * DV],      \
+        v2_[kTile * DV];                                                                  \
+    __shared__ __attribute__((aligned(16))) float l0_[kTile], l1_[kTile], l2_[kTile];    \
+    __shared__ __attribute__((aligned(16))) float t0_[3 * kTile], t1_[3 * kTile],        \
+        t2_[3 * kTile];                                                                   \
+    __shared__ __attribute__((aligned(16))) bf16_t ps_[kTile * C64<DK, DV>::PP];          \
+    __shared__ __attribute__((aligned(16))) float sink_[kTile];                           \
+    __shared__ __attribute__((aligned(16))) bf16_t g_[kTile * DV];                        \
+    __shared__ __attribute__((aligned(16))) float aff_[2 * DV];                           \
+    const Lds<DK, DV> L{{q0_, q1_, nullptr}, {k0_, k1_, k2_}, {v0_, v1_, v2_},            \
+                        {l0_, l1_, l2_}, {t0_, t1_, t2_}, ps_, sink_, g_, aff_};
+
+template <int DK, int DV, bool GATED>
+__device__ inline void main_pass(const Params& p, const Lds<DK, DV>& L) {
     zero_upper_blocks<DK, DV>(L.ps);
     const SegPlan& pl = p.plan;
     const int64_t gidx = blockIdx.x;
@@ -649,16 +811,15 @@ __global__ __launch_bounds__(kThreadsFor<DV>) void prefill_main_c64_kernel(Param
         const int64_t slot = initial ? 0 : gidx - seg_first_inner(pl, x) + 1;
         load_state<DK, DV>(a, initial && p.state_in ? p.state_in + x * DK * DV : nullptr);
         int64_t lead = 0;
-        const float total = run_chunks<DK, DV>(p, L, x, cb, ce, initial, a, &lead);
+        const float total = run_chunks<DK, DV, GATED>(p, L, x, cb, ce, initial, a, &lead);
         save_state<DK, DV>(a, p.ws_state + (x * pl.max_seg + slot) * (int64_t)(DK * DV));
         if (threadIdx.x == 0) p.ws_meta[x * pl.max_seg + slot] = make_float2(total, (float)lead);
         t = x * pl.nc + ce;
     }
 }
 
-template <int DK, int DV>
-__global__ __launch_bounds__(kThreadsFor<DV>) void prefill_prefix_c64_kernel(Params p) {
-    GRET_C64_LDS(DK, DV)
+template <int DK, int DV, bool GATED>
+__device__ inline void prefix_pass(const Params& p, const Lds<DK, DV>& L) {
     const SegPlan& pl = p.plan;
     const int64_t gidx = blockIdx.x;
     const int64_t lo = seg_lo(pl, gidx);
@@ -672,30 +833,62 @@ __global__ __launch_bounds__(kThreadsFor<DV>) void prefill_prefix_c64_kernel(Par
     Acc<DK, DV> a;
     load_state<DK, DV>(a, p.ws_state + (x * pl.max_seg + slot) * (int64_t)(DK * DV));
     int64_t unused = 0;
-    run_chunks<DK, DV, true>(p, L, x, cb, cb + lead, true, a, &unused);
+    run_chunks<DK, DV, GATED, true>(p, L, x, cb, cb + lead, true, a, &unused);
 }
+
+template <int DK, int DV, bool GATED>
+__global__ __launch_bounds__(kThreadsFor<DV>) void prefill_main_c64_kernel(Params p) {
+    if constexpr (GATED) {
+        GRET_C64_LDS_GATED(DK, DV)
+        main_pass<DK, DV, true>(p, L);
+    } else {
+        GRET_C64_LDS(DK, DV)
+        main_pass<DK, DV, false>(p, L);
+    }
+}
+
+template <int DK, int DV, bool GATED>
+__global__ __launch_bounds__(kThreadsFor<DV>) void prefill_prefix_c64_kernel(Params p) {
+    if constexpr (GATED) {
+        GRET_C64_LDS_GATED(DK, DV)
+        prefix_pass<DK, DV, true>(p, L);
+    } else {
+        GRET_C64_LDS(DK, DV)
+        prefix_pass<DK, DV, false>(p, L);
+    }
+}
+#undef GRET_C64_LDS_GATED
 #undef GRET_C64_LDS
 
-template <int DK, int DV>
-hipError_t launch(const PrefillArgs& a, const SegPlan& plan) {
+template <int DK, int DV, bool GATED>
+hipError_t launch_g(const PrefillArgs& a, const SegPlan& plan) {
     const Params p = make_params(a, plan, DK, DV);
-    hipLaunchKernelGGL((prefill_main_c64_kernel<DK, DV>), dim3(plan.G), dim3(C64<DK, DV>::NT), 0,
-                       a.stream, p);
+    hipLaunchKernelGGL((prefill_main_c64_kernel<DK, DV, GATED>), dim3(plan.G),
+                       dim3(C64<DK, DV>::NT), 0, a.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_combine<DK, DV>(p, a.stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_prefix_c64_kernel<DK, DV>), dim3(plan.G), dim3(C64<DK, DV>::NT), 0,
-                       a.stream, p);
+    hipLaunchKernelGGL((prefill_prefix_c64_kernel<DK, DV, GATED>), dim3(plan.G),
+                       dim3(C64<DK, DV>::NT), 0, a.stream, p);
     return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch(const PrefillArgs& a, const SegPlan& plan) {
+    return a.epi.gate ? launch_g<DK, DV, true>(a, plan) : launch_g<DK, DV, false>(a, plan);
 }
 
 template <int DK, int DV>
 int blocks_per_cu() {
     int n = 0;
+    int ng = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &n, prefill_main_c64_kernel<DK, DV>, C64<DK, DV>::NT, 0);
-    return e == hipSuccess ? n : 0;
+        &n, prefill_main_c64_kernel<DK, DV, false>, C64<DK, DV>::NT, 0);
+    const hipError_t eg = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &ng, prefill_main_c64_kernel<DK, DV, true>, C64<DK, DV>::NT, 0);
+    // the plan is shared by the plain and the gated kernels
+    return e == hipSuccess && eg == hipSuccess ? (n < ng ? n : ng) : 0;
 }
 
 }  // namespace

@@ -44,6 +44,13 @@ struct Params {
     float2* ws_meta;  // [BH][max_seg]: (total log-decay, leading chunks)
     SegPlan plan;
     int64_t N;
+    // output epilogue applied in the kernel's output store (chunk 64 only):
+    // gate [BH][N][DV] and the per-head affine [H][DV] (null: 1 and 0)
+    const bf16_t* gate;
+    const float* gate_w;
+    const float* gate_b;
+    float eps;
+    int64_t H;
 };
 
 inline Params make_params(const PrefillArgs& a, const SegPlan& plan, int64_t dk, int64_t dv) {
@@ -60,6 +67,11 @@ inline Params make_params(const PrefillArgs& a, const SegPlan& plan, int64_t dk,
     p.ws_meta = reinterpret_cast<float2*>(static_cast<char*>(a.workspace) + lay.meta_off);
     p.plan = plan;
     p.N = a.N;
+    p.gate = static_cast<const bf16_t*>(a.epi.gate);
+    p.gate_w = a.epi.weight;
+    p.gate_b = a.epi.bias;
+    p.eps = a.epi.eps;
+    p.H = a.H;
     return p;
 }
 
