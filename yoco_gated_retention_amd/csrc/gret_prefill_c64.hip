@@ -643,10 +643,11 @@ __device__ inline void chunk(const Lds<DK, DV>& L, const HeadRsrc& hr,
     const float gc = tv.beta[kTile - 1];
     total += gc;
     next_full = all_full || total < kSurvivalDropLog;
-    // The DMA of tile k + 2 is issued in three parts spread over the chunk
-    // (queries, keys, then values and log-gates, always in that order), so that
-    // the eight wavefronts' memory instructions do not queue up behind each
-    // other at the start of the chunk.
+    // The DMA of tile k + 2 is issued in parts spread over the chunk (plain:
+    // queries, keys, then values and log-gates; gated: keys, then queries,
+    // values and log-gates; always in that order), so that the eight
+    // wavefronts' memory instructions do not queue up behind each other at the
+    // start of the chunk.
     constexpr int Y = (X + 2) % 3;
     if constexpr (GATED) {
         flush_tile_gated<DK, DV>(L.v[Y], L.gt, L.aff, prev_out, pos - kTile, eps);
