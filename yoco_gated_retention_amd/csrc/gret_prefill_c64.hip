@@ -621,10 +621,13 @@ __device__ inline void wait_tile(int k) {
 // flushed tile in the gate buffer (loaded one chunk earlier, right after that
 // chunk's flush). The queries are double-buffered (QX = k % 2) to make room
 // for it, so the DMA of tile k + 2's queries waits until every wavefront is
-// done with tile k's scores. Per chunk each wavefront then issues: ST stores,
-// VB gate loads, then QB keys, QB queries, VB values and 1 log-gate load for
-// tile k + 2; the wait at the chunk start leaves only the last DMA of those
-// outstanding, so the gate of tile k - 1 and all of tile k have landed.
+// done with tile k's scores. Per chunk each wavefront issues: QB keys of tile
+// k + 2 (before the epilogue's vector work, so that they are in flight
+// early), ST stores, VB gate loads, VB values and 1 log-gate load of tile
+// k + 2 (into the rows this wavefront has just flushed), then QB queries of
+// tile k + 2. The wait at the chunk start leaves the values, log-gates and
+// queries of the previous chunk outstanding, so the gate of tile k - 1 and all
+// of tile k have landed.
 template <int DK, int DV, int X, int QX, bool GATED>
 __device__ inline void chunk(const Lds<DK, DV>& L, const HeadRsrc& hr,
                              const __amdgpu_buffer_rsrc_t& gate_r,
@@ -634,7 +637,7 @@ __device__ inline void chunk(const Lds<DK, DV>& L, const HeadRsrc& hr,
                              Acc<DK, DV>& a) {
     using c = C64<DK, DV>;
     if constexpr (GATED)
-        wait_vm<c::DMA>();
+        wait_vm<c::DMA - c::QB>();
     else
         wait_tile<DK, DV>(k);
     if (threadIdx.x < 64) tables_from_lds(L.ell[X], L.tab[X]);
@@ -643,27 +646,28 @@ __device__ inline void chunk(const Lds<DK, DV>& L, const HeadRsrc& hr,
     const float gc = tv.beta[kTile - 1];
     total += gc;
     next_full = all_full || total < kSurvivalDropLog;
-    // The DMA of tile k + 2 is issued in parts spread over the chunk (plain:
-    // queries, keys, then values and log-gates; gated: keys, then queries,
-    // values and log-gates; always in that order), so that the eight
-    // wavefronts' memory instructions do not queue up behind each other at the
-    // start of the chunk.
+    // The plain kernels issue the DMA of tile k + 2 in three parts spread
+    // over the chunk (queries, keys, then values and log-gates, always in that
+    // order), so that the eight wavefronts' memory instructions do not queue up
+    // behind each other at the start of the chunk. The gated kernels' order is
+    // given above.
     constexpr int Y = (X + 2) % 3;
     if constexpr (GATED) {
+        dma_k<DK, DV, Y>(L, hr, pos + 2 * kTile);
         flush_tile_gated<DK, DV>(L.v[Y], L.gt, L.aff, prev_out, pos - kTile, eps);
         dma_gate<DK, DV>(L.gt, full ? gate_r : no_q, pos);
+        dma_v_ell<DK, DV, Y>(L, hr, no_q, pos + 2 * kTile);
     } else {
         if (k > 0) flush_tile<DK, DV>(L.v[Y], prev_out, pos - kTile);
         dma_q<DK, DV, Y>(L, next_full ? hr.q : no_q, pos + 2 * kTile);
     }
     f32x4 o[c::CT][4];
     if (full) cross_term<DK, DV, GATED>(tv, a, o);
-    dma_k<DK, DV, Y>(L, hr, pos + 2 * kTile);
+    if constexpr (!GATED) dma_k<DK, DV, Y>(L, hr, pos + 2 * kTile);
     if (full) scores_diag<DK, DV, GATED>(tv, L.ps);
     if constexpr (GATED) {
         if (full) lds_barrier();
         dma_q<DK, DV, QX>(L, next_full ? hr.q : no_q, pos + 2 * kTile);
-        dma_v_ell<DK, DV, Y>(L, hr, no_q, pos + 2 * kTile);
         if (full) apply_scores<DK, DV, GATED>(L.ps, tv.vs, o);
     } else {
         dma_v_ell<DK, DV, Y>(L, hr, no_q, pos + 2 * kTile);
