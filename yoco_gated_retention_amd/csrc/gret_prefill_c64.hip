@@ -543,7 +543,10 @@ __device__ inline void dma_gate(bf16_t* gt, const __amdgpu_buffer_rsrc_t& g, uin
 // element-wise gate swish(X W_G)). Lane i holds 8 channels of one row, a row's
 // DV / 8 lanes are adjacent, so mean and variance (two passes, fp32) are
 // reductions inside a lane group; the gate piece sits at the same LDS offset
-// in the gate buffer, the affine of the piece's channels in aff.
+// in the gate buffer, the affine of the piece's channels in aff. As in
+// flush_tile, the DMAs issued right after it (the next gate tile and the next
+// V tile) overwrite only this wavefront's blocks, whose LDS reads have
+// completed because the stores consume them.
 //   y = swish(gate) * ((o - mean) / sqrt(var + eps) * w + b)
 template <int DK, int DV>
 __device__ inline void flush_tile_gated(const bf16_t* vs, const bf16_t* gt, const float* aff,
