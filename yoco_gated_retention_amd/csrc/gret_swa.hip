@@ -11,9 +11,11 @@
 // leaves each layer's last W keys and values in a fixed buffer.
 //
 // Prefill, per (sequence, query head, 256-query tile): 8 wavefronts own 32
-// queries each. Keys and values stream through LDS in 64-position stages
-// (three stages, filled by direct buffer-to-LDS loads two stages ahead) over
-// the tile's joint window. A wavefront computes S^T = K Q^T with
+// queries each. Keys and values stream through LDS in two stages of 128
+// positions (two 64-key blocks each) over the tile's joint window: a stage is
+// refilled by direct buffer-to-LDS loads as soon as every wavefront has
+// consumed it, so the loads run one stage (two blocks) ahead with one
+// workgroup barrier per 128 keys. A wavefront computes S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (Q^T stays in registers), so each lane holds 16
 // scores of one query and the other half-wave the other 16 of the 32 keys:
 // the online softmax needs one cross-lane exchange per block. The
@@ -32,8 +34,8 @@ namespace {
 constexpr int kSWaves = 8;
 constexpr int kSThreads = 64 * kSWaves;
 constexpr int kSQ = 32 * kSWaves;  // queries per workgroup
-constexpr int kSK = 64;            // keys per LDS stage
-constexpr int kSStages = 3;        // LDS stages (3 or 4), filled kSStages - 1 blocks ahead
+constexpr int kSK = 64;            // keys per block (one softmax update)
+constexpr int kSBlocks = 2;        // blocks per LDS stage; two stages, refilled one stage ahead
 constexpr int kXcds = 8;
 
 
@@ -65,13 +67,13 @@ template <int D>
 struct SCfg {
     static constexpr int KS = D / 16;               // k-steps of S^T = K Q^T
     static constexpr int CB = D / 32;               // 32-channel blocks of O^T
-    static constexpr int TILE = kSK * D;            // elements per K or V stage
+    static constexpr int TILE = kSBlocks * kSK * D;  // elements per K or V stage
     static constexpr int BLK = TILE * 2 / 1024;     // 1 KB loads per K or V stage
     static constexpr int PER_WAVE = BLK / kSWaves;  // of each, per wavefront
     static constexpr int DMA = 2 * PER_WAVE;        // loads per wavefront and stage
 };
 
-// One 1 KB direct load of a 64-position tile: lane i fills LDS byte 16 i of
+// One 1 KB direct load of a stage of kSBlocks * 64 positions: lane i fills LDS byte 16 i of
 // block blk = row (512 / D) blk + i / (D / 8), slot i % (D / 8), from the
 // global chunk slot ^ swizzle of that position.
 template <int D, bool IS_V>
@@ -99,27 +101,19 @@ __device__ inline void dma_stage(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc
 // The key/value stages in LDS (file scope, so that every helper names
 // the object it touches and the compiler can tell the stages apart when it
 // orders LDS reads after the direct loads into other stages); sized for d = 128.
-__shared__ __attribute__((aligned(1024))) bf16_t swa_k0[kSK * 128];
-__shared__ __attribute__((aligned(1024))) bf16_t swa_v0[kSK * 128];
-__shared__ __attribute__((aligned(1024))) bf16_t swa_k1[kSK * 128];
-__shared__ __attribute__((aligned(1024))) bf16_t swa_v1[kSK * 128];
-__shared__ __attribute__((aligned(1024))) bf16_t swa_k2[kSK * 128];
-__shared__ __attribute__((aligned(1024))) bf16_t swa_v2[kSK * 128];
-__shared__ __attribute__((aligned(1024))) bf16_t swa_k3[kSK * 128];
-__shared__ __attribute__((aligned(1024))) bf16_t swa_v3[kSK * 128];
+__shared__ __attribute__((aligned(1024))) bf16_t swa_k0[kSBlocks * kSK * 128];
+__shared__ __attribute__((aligned(1024))) bf16_t swa_v0[kSBlocks * kSK * 128];
+__shared__ __attribute__((aligned(1024))) bf16_t swa_k1[kSBlocks * kSK * 128];
+__shared__ __attribute__((aligned(1024))) bf16_t swa_v1[kSBlocks * kSK * 128];
 template <int X>
 __device__ inline bf16_t* swa_kst() {
     if constexpr (X == 0) return swa_k0;
-    if constexpr (X == 1) return swa_k1;
-    if constexpr (X == 2) return swa_k2;
-    return swa_k3;
+    return swa_k1;
 }
 template <int X>
 __device__ inline bf16_t* swa_vst() {
     if constexpr (X == 0) return swa_v0;
-    if constexpr (X == 1) return swa_v1;
-    if constexpr (X == 2) return swa_v2;
-    return swa_v3;
+    return swa_v1;
 }
 
 struct SwaParams {
@@ -241,29 +235,33 @@ __device__ inline void swa_block(const bf16_t* kt, const bf16_t* vt, const bf16x
         }
 }
 
-// One pipeline step over the block i of n (stage X of kSStages): wait for its
-// loads, refill the stage read one step ago with block i + kSStages - 1,
-// compute. Loads are issued unconditionally so that the compiler's own waits
-// stay out of the loop: with the refill under a branch it made the reads of
-// one stage in every round wait for all loads in flight.
+// One pipeline step over stage t (LDS stage X = t % 2, blocks 2t and 2t + 1
+// of n): wait for its loads, then, once every wavefront has finished the
+// stage before, refill that stage's buffers with stage t + 1 and compute.
+// Loads are issued unconditionally so that the compiler's own waits stay out
+// of the loop: with the refill under a branch it made the reads of one stage
+// wait for all loads in flight. Blocks past the window are loaded too (rows
+// past the head read zeros) and never used.
 template <int D, int X>
-__device__ inline void swa_step(int i, int n,
-                                int64_t kb0, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                const bf16x8 (&qf)[SCfg<D>::KS], int64_t qi, int64_t qw0,
-                                int64_t W, float cl, SwaAcc<D>& st) {
-    constexpr int AHEAD = kSStages - 1;
-    // blocks past the window are loaded too (rows past the head read zeros)
-    // and never used: every step issues the same loads, so the waits are fixed
-    wait_vm<(AHEAD - 1) * SCfg<D>::DMA>();
+__device__ inline void swa_step(int t, int n, int64_t kb0, __amdgpu_buffer_rsrc_t kr,
+                                __amdgpu_buffer_rsrc_t vr, const bf16x8 (&qf)[SCfg<D>::KS],
+                                int64_t qi, int64_t qw0, int64_t W, float cl, SwaAcc<D>& st) {
+    wait_vm<0>();
     lds_barrier();
-    dma_stage<D>(kr, vr, swa_kst<(X + AHEAD) % kSStages>(), swa_vst<(X + AHEAD) % kSStages>(),
-                 static_cast<uint32_t>((kb0 + i + AHEAD) * kSK));
-    const int64_t key0 = (kb0 + i) * kSK;
-    // this wavefront's queries qw0 .. qw0 + 31 see keys qw0 - W + 1 .. qw0 + 31
-    const bool active = key0 + kSK > qw0 - W + 1 && key0 <= qw0 + 31;
-    if (active) {
-        const bool inside = key0 + kSK - 1 <= qw0 && key0 >= qw0 + 31 - W + 1;
-        swa_block<D>(swa_kst<X>(), swa_vst<X>(), qf, key0, qi, W, !inside, cl, st);
+    dma_stage<D>(kr, vr, swa_kst<X ^ 1>(), swa_vst<X ^ 1>(),
+                 static_cast<uint32_t>((kb0 + kSBlocks * (t + 1)) * kSK));
+#pragma unroll
+    for (int hb = 0; hb < kSBlocks; ++hb) {
+        const int i = kSBlocks * t + hb;
+        const int64_t key0 = (kb0 + i) * kSK;
+        // this wavefront's queries qw0 .. qw0 + 31 see keys qw0 - W + 1 .. qw0 + 31
+        const bool active = i < n && key0 + kSK > qw0 - W + 1 && key0 <= qw0 + 31;
+        if (active) {
+            const bool inside = key0 + kSK - 1 <= qw0 && key0 >= qw0 + 31 - W + 1;
+            swa_block<D>(swa_kst<X>() + hb * kSK * D, swa_vst<X>() + hb * kSK * D, qf, key0, qi, W,
+                         !inside, cl, st);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -311,21 +309,13 @@ __global__ __launch_bounds__(kSThreads) void swa_prefill_kernel(SwaParams p) {
     const float cl = p.scale_log2;
 
     dma_stage<D>(kr, vr, swa_kst<0>(), swa_vst<0>(), static_cast<uint32_t>(kb0 * kSK));
-    dma_stage<D>(kr, vr, swa_kst<1>(), swa_vst<1>(), static_cast<uint32_t>((kb0 + 1) * kSK));
-    if (kSStages > 3 && n > 2)
-        dma_stage<D>(kr, vr, swa_kst<2>(), swa_vst<2>(), static_cast<uint32_t>((kb0 + 2) * kSK));
-#define GRET_SWA_STEP(X) swa_step<D, X>(i + X, n, kb0, kr, vr, qf, qi, qw0, W, cl, st)
-    int i = 0;
-    for (; i + kSStages <= n; i += kSStages) {
-        GRET_SWA_STEP(0);
-        GRET_SWA_STEP(1);
-        GRET_SWA_STEP(2);
-        if constexpr (kSStages > 3) GRET_SWA_STEP(3);
+    const int stages = (n + kSBlocks - 1) / kSBlocks;
+    int t = 0;
+    for (; t + 2 <= stages; t += 2) {
+        swa_step<D, 0>(t, n, kb0, kr, vr, qf, qi, qw0, W, cl, st);
+        swa_step<D, 1>(t + 1, n, kb0, kr, vr, qf, qi, qw0, W, cl, st);
     }
-    if (i < n) GRET_SWA_STEP(0);
-    if (i + 1 < n) GRET_SWA_STEP(1);
-    if (kSStages > 3 && i + 2 < n) GRET_SWA_STEP(2);
-#undef GRET_SWA_STEP
+    if (t < stages) swa_step<D, 0>(t, n, kb0, kr, vr, qf, qi, qw0, W, cl, st);
     wait_vm<0>();  // the loads past the window have landed before the LDS is released
 
     if (qi >= N) return;
