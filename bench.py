@@ -167,7 +167,7 @@ def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir, mfma_dir=None):
             continue
         if which == "prefill_gated":
             # the combine launch is shared by the plain and the gated prefill
-            names += sorted(k for k in fetch if "combine" in k)
+            names += sorted(k for k in fetch if "prefill_combine" in k)
         kern = {}
         for k in names:
             kern[short_kernel_name(k)] = {

@@ -92,6 +92,25 @@ def test_summarize_pmc_scales_by_the_copy_calibration(tmp_path, capsys):
     assert "decode" not in out  # no dispatches of it in these tables
 
 
+def test_summarize_pmc_gated_prefill_takes_only_the_prefill_combine(tmp_path, capsys):
+    gmain = "gret::prefill_main_c64_kernel<128, 128, true>(Params)"
+    comb = "gret::prefill_combine_kernel<128, 128>(Params)"
+    xcomb = "gret::xattn_combine_kernel<128>(XParams)"
+    copy = "copy_kernel(float4 const*, float4*, long)"
+    rows = [(gmain, 400.0), (comb, 10.0), (xcomb, 7.0)]
+    fetch = _pmc_dir(str(tmp_path / "f"), [(k, "FETCH_SIZE", v) for k, v in rows])
+    write = _pmc_dir(str(tmp_path / "w"), [(k, "WRITE_SIZE", v) for k, v in rows])
+    cf = _pmc_dir(str(tmp_path / "cf"), [(copy, "FETCH_SIZE", 524288.0)])
+    cw = _pmc_dir(str(tmp_path / "cw"), [(copy, "WRITE_SIZE", 1048576.0)])
+    bench.summarize_pmc(fetch, write, cf, cw)
+    out = json.loads(capsys.readouterr().out)
+    gated = out["prefill_gated"]["kernels"]
+    assert sorted(gated) == ["gret::prefill_combine_kernel<128, 128>",
+                             "gret::prefill_main_c64_kernel<128, 128, true>"]
+    assert out["prefill_gated"]["fetch_bytes"] == (400.0 + 10.0) * 1024 * 2.0
+    assert out["xattn"]["fetch_bytes"] == 7.0 * 1024 * 2.0
+
+
 def test_recorded_counters_need_matching_sources(tmp_path, monkeypatch):
     rec = {"prefill": {"sources_sha256": bench.sources_sha256("prefill"),
                        "fetch_bytes": 10.0, "write_bytes": 3.0,
