@@ -5,7 +5,8 @@ The header is compiled with g++ into a small driver that enumerates, for many
 visits and the slot it writes, and the count the combine kernel reads. They are
 checked here by brute force: slots are unique, in range (below the per-head
 bound that sizes the workspace), in sequence order, and every (head, chunk)
-pair is covered exactly once.
+pair is covered exactly once. The map from a workgroup's launch index to its
+segment (contiguous segment runs per XCD) must be a bijection.
 """
 import os
 import subprocess
@@ -39,6 +40,7 @@ int main(int argc, char** argv) {
         }
     }
     for (int64_t x = 0; x < p.BH; ++x) printf("C %lld %lld\n", (long long)x, (long long)seg_count(p, x));
+    for (int64_t b = 0; b < p.G; ++b) printf("B %lld %lld\n", (long long)b, (long long)seg_of_block(p.G, b));
     return 0;
 }
 """
@@ -70,6 +72,7 @@ def test_segments_cover_and_slots(driver, BH, nc, G):
     covered = {}
     slots = {}
     counts = {}
+    seg_of = {}
     for line in out[1:]:
         if line.startswith("S "):
             g, x, cb, ce, slot = map(int, line.split()[1:])
@@ -83,7 +86,18 @@ def test_segments_cover_and_slots(driver, BH, nc, G):
         elif line.startswith("C "):
             x, n = map(int, line.split()[1:])
             counts[x] = n
+        elif line.startswith("B "):
+            b, g = map(int, line.split()[1:])
+            seg_of[b] = g
     assert len(covered) == BH * nc
+    # the launch-index -> segment map is a bijection of [0, G), and the ids
+    # that share an XCD (b mod 8) take one contiguous run of segments in order
+    assert sorted(seg_of) == list(range(Geff)) and sorted(seg_of.values()) == list(range(Geff))
+    for xcd in range(8):
+        run = [seg_of[b] for b in range(xcd, Geff, 8)]
+        assert run == list(range(run[0], run[0] + len(run))) if run else True
+    starts = sorted(seg_of[b] for b in range(min(8, Geff)))
+    assert starts[0] == 0
     for x in range(BH):
         segs = sorted((s, cb, ce) for (xx, s), (cb, ce) in slots.items() if xx == x)
         assert counts[x] == len(segs) <= max_seg

@@ -450,7 +450,8 @@ template <int DK, int DV, int R>
 __global__ __launch_bounds__(kThreadsFor<DV>) void prefill_main_kernel(Params p) {
     __shared__ Smem<DK, DV, R> sm;
     const SegPlan& pl = p.plan;
-    const int64_t gidx = blockIdx.x;
+    // each XCD streams one contiguous range of the heads' chunk sequences
+    const int64_t gidx = seg_of_block(pl.G, blockIdx.x);
     const int64_t hi = seg_lo(pl, gidx + 1);
     int64_t t = seg_lo(pl, gidx);
     Acc<DK, DV, R> a;

@@ -807,7 +807,8 @@ template <int DK, int DV, bool GATED>
 __device__ inline void main_pass(const Params& p, const Lds<DK, DV>& L) {
     zero_upper_blocks<DK, DV>(L.ps);
     const SegPlan& pl = p.plan;
-    const int64_t gidx = blockIdx.x;
+    // each XCD streams one contiguous range of the heads' chunk sequences
+    const int64_t gidx = seg_of_block(pl.G, blockIdx.x);
     const int64_t hi = seg_lo(pl, gidx + 1);
     int64_t t = seg_lo(pl, gidx);
     Acc<DK, DV> a;

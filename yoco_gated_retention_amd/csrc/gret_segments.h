@@ -59,6 +59,21 @@ GRET_HD int64_t seg_count(const SegPlan& p, int64_t x) {
     return 1 + (b > a ? b - a : 0);
 }
 
+// Segment of the workgroup with launch index b. The hardware hands workgroup
+// ids to the chip's XCDs round-robin (id mod kXcds), and each XCD has its own
+// L2 and address-translation caches. So that XCD x works on one contiguous
+// range of the (head, chunk) order, the ids that land on XCD x take segments
+// start(x), start(x) + 1, ... in launch order. A bijection of [0, G) for any
+// G: the ids with b mod kXcds == x number per + (x < rem), per = G / kXcds,
+// rem = G mod kXcds, and XCD x's range starts at x * per + min(x, rem).
+constexpr int64_t kXcds = 8;
+
+GRET_HD int64_t seg_of_block(int64_t G, int64_t b) {
+    const int64_t x = b % kXcds, local = b / kXcds;
+    const int64_t per = G / kXcds, rem = G % kXcds;
+    return x * per + (x < rem ? x : rem) + local;
+}
+
 // Upper bound on seg_count over all heads for a given G: one head-initial
 // segment plus at most ceil(G / BH) inner starts (an open interval of G/BH
 // consecutive g values), and never more than nc segments.
