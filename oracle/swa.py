@@ -45,26 +45,48 @@ def _attend(qv, ks, vs, scale):
     return (p / p.sum()) @ vs
 
 
-def oracle_swa_prefill_f64(q, k, v, window, scale=None):
+def oracle_swa_prefill_f64(q, k, v, window, scale=None, rows=None):
     """Sliding-window causal attention of every query position (float64), one
-    query row at a time over the keys of its own window."""
+    query row at a time over the keys of its own window.
+
+    rows: optional 1-D sequence of query positions; then only those rows are
+    computed (each exactly as above) and out is [B, Hq, len(rows), d], row r
+    of it being position rows[r]. q may then hold just those rows
+    ([B, Hq, len(rows), d]) or the whole prompt ([B, Hq, N, d])."""
     qd, kd, vd = _widen(q), _widen(k), _widen(v)
-    B, Hq, N, d = qd.shape
-    _, Hkv, Nk, dk = kd.shape
-    if Nk != N or dk != d or vd.shape[:3] != (B, Hkv, N):
+    B, Hq, Nq, d = qd.shape
+    _, Hkv, N, dk = kd.shape
+    if dk != d or vd.shape[:3] != (B, Hkv, N):
         raise ValueError("shape mismatch")
     if Hq % Hkv != 0 or window < 1:
         raise ValueError("Hq must be a multiple of Hkv and the window positive")
+    if rows is None:
+        pos = np.arange(N)
+        if Nq != N:
+            raise ValueError("shape mismatch")
+        qrow = pos
+    else:
+        pos = np.asarray(rows, dtype=np.int64).reshape(-1)
+        if pos.size and (pos.min() < 0 or pos.max() >= N):
+            raise ValueError("rows out of range")
+        if Nq == pos.size:
+            qrow = np.arange(pos.size)
+        elif Nq == N:
+            qrow = pos
+        else:
+            raise ValueError("q must hold the listed rows or the whole prompt")
     G = Hq // Hkv
     if scale is None:
         scale = 1.0 / np.sqrt(d)
-    out = np.zeros((B, Hq, N, vd.shape[3]), dtype=np.float64)
+    out = np.zeros((B, Hq, pos.size, vd.shape[3]), dtype=np.float64)
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            for i in range(N):
+            for r in range(pos.size):
+                i = int(pos[r])
                 j0 = max(0, i - window + 1)
-                out[b, h, i] = _attend(qd[b, h, i], kd[b, g, j0:i + 1], vd[b, g, j0:i + 1], scale)
+                out[b, h, r] = _attend(qd[b, h, qrow[r]], kd[b, g, j0:i + 1], vd[b, g, j0:i + 1],
+                                       scale)
     return out
 
 

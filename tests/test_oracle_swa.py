@@ -38,6 +38,27 @@ def test_prefill_matches_torch_window_mask(N, window, Hq, Hkv):
     np.testing.assert_allclose(got, sdpa_window(q, k, v, window), rtol=1e-10, atol=1e-12)
 
 
+def test_prefill_selected_rows_match_torch_window_mask():
+    """The rows option (used where only sampled outputs of a long prompt are
+    checked): every listed row equals the same row of torch's masked attention,
+    whether q holds the whole prompt or only the listed rows."""
+    rng = np.random.default_rng(77)
+    N, d, C, Hq, Hkv = 90, 8, 16, 4, 2
+    q = rng.standard_normal((2, Hq, N, d))
+    k = rng.standard_normal((2, Hkv, N, d))
+    v = rng.standard_normal((2, Hkv, N, d))
+    rows = np.array([0, 1, 15, 16, 17, 50, 89])
+    ref = sdpa_window(q, k, v, C)[:, :, rows]
+    np.testing.assert_allclose(oracle_swa_prefill_f64(q, k, v, C, rows=rows), ref,
+                               rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(oracle_swa_prefill_f64(q[:, :, rows], k, v, C, rows=rows), ref,
+                               rtol=1e-10, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle_swa_prefill_f64(q, k, v, C, rows=[N])
+    with pytest.raises(ValueError):
+        oracle_swa_prefill_f64(q[:, :, :5], k, v, C, rows=rows)
+
+
 def test_prefill_explicit_loops_tiny():
     rng = np.random.default_rng(5)
     N, d, C = 9, 3, 4

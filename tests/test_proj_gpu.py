@@ -129,7 +129,7 @@ def test_projection_large_logits(gret):
 def test_projection_full_size_sampled(gret):
     """The benchmark's shape (B=1, N=524288, D=3072, 24 heads of 128, gate),
     inputs drawn on the device by a seeded generator; the oracle recomputes
-    2048 sampled tokens (the first and last tiles' edges included)."""
+    16384 sampled tokens (the first and last tiles' edges included)."""
     B, N, D, H, dk = 1, 524288, 3072, 24, 128
     say("head_projection full size B=%d N=%d D=%d H=%d dk=%d" % (B, N, D, H, dk))
     g = torch.Generator(device="cuda").manual_seed(6006)
@@ -140,7 +140,7 @@ def test_projection_full_size_sampled(gret):
     torch.cuda.synchronize()
     rng = np.random.default_rng(1)
     idx = np.unique(np.concatenate([np.arange(0, 8), np.arange(N - 8, N), [255, 256, 257],
-                                    rng.integers(0, N, 2048 - 19)]))
+                                    rng.integers(0, N, 16384 - 19)]))
     ti = torch.from_numpy(idx).cuda()
     xs = to_host(x[0, ti].contiguous())[None]
     k_ref, lg_ref = oracle_head_projection_f64(xs, to_host(wk), to_host(wg),
