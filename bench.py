@@ -242,15 +242,24 @@ def to_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def time_calls(fn, steps, warmup):
-    """Runs fn warmup times, synchronises, then times `steps` back-to-back calls
-    on the current stream with one HIP event before each call and one after the
-    last. Returns (mean ms over the block, median ms of the calls, per-call ms)."""
+def time_calls(fn, steps, warmup, warm_s=0.0):
+    """Runs fn warmup times (and, with warm_s > 0, keeps calling it until warm_s
+    seconds have passed: a short call after an idle stretch, such as a CPU
+    leg, otherwise runs on clocks that are still ramping up), synchronises,
+    then times `steps` back-to-back calls on the current stream with one HIP
+    event before each call and one after the last. Returns (mean ms over the
+    block, median ms of the calls, per-call ms)."""
     import torch
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    if warm_s > 0:
+        t0 = time.time()
+        while time.time() - t0 < warm_s:
+            for _ in range(8):
+                fn()
+            torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     for i in range(steps):
@@ -298,8 +307,8 @@ class DevicePrefill:
         return lambda: self.gret.gret_prefill(self.q, self.k, self.v, self.lg, self.si, chunk=chunk,
                                               out=self.out, state_out=self.so, workspace=ws)
 
-    def time(self, chunk, steps, warmup):
-        return time_calls(self.call(chunk), steps, warmup)
+    def time(self, chunk, steps, warmup, warm_s=0.0):
+        return time_calls(self.call(chunk), steps, warmup, warm_s)
 
     def free(self):
         import torch
@@ -942,12 +951,13 @@ def bench_prefill_legs(gret, dev, args):
     dp2 = DevicePrefill(gret, d2, dev)
     sw2 = []
     for ch in (64, 128, 256):
-        _, m, _ = dp2.time(ch, 20, 3)
+        _, m, _ = dp2.time(ch, 20, 3, warm_s=0.25)
         sw2.append({"chunk": ch, "ms_median": m, "tokens_per_s": c2["N"] / (m * 1e-3),
                     "roofline": prefill_roofline(1, c2["H"], c2["N"], c2["dk"], c2["dv"], ch,
                                                  False, m, kern, meas, meas_seg)})
     dp2.free()
-    res["prefill_32k_chunk_sweep"] = {"workload": c2["name"], "timing": "median of 20 calls",
+    res["prefill_32k_chunk_sweep"] = {"workload": c2["name"],
+                                      "timing": "median of 20 calls after 0.25 s of warm-up calls",
                                       "chunks": sw2}
     log("32K chunk sweep (ms): %s" % ", ".join("%d: %.4f" % (x["chunk"], x["ms_median"])
                                                 for x in sw2))
@@ -990,7 +1000,7 @@ def bench_tiny_f32(gret, dev, args):
     c1 = CONFIGS["tiny_f32"]
     d = make_prefill_inputs("tiny_f32")
     dp = DevicePrefill(gret, d, dev)
-    _, m, _ = dp.time(64, 20, 3)
+    _, m, _ = dp.time(64, 20, 3, warm_s=0.25)
     steps = c1["decode_steps"]
     toks = [[to_dev(d[x][t], dev) for x in ("dec_q", "dec_k", "dec_v", "dec_log_gamma")]
             for t in range(steps)]
@@ -1001,11 +1011,11 @@ def bench_tiny_f32(gret, dev, args):
         for t in range(steps):
             gret.gret_decode_step(*toks[t], state, out=out)
 
-    _, md, _ = time_calls(decode_all, 10, 2)
+    _, md, _ = time_calls(decode_all, 10, 2, warm_s=0.25)
     dp.free()
     res = {"workload": c1["name"], "prefill_ms_median": m, "tokens_per_s": c1["N"] / (m * 1e-3),
            "decode_us_per_step": 1000.0 * md / steps, "timing": "median of 20 prefills; median "
-           "of 10 runs of the 16 decode steps"}
+           "of 10 runs of the 16 decode steps (each after 0.25 s of warm-up calls)"}
     if not args.skip_cpu:
         t0, n = time.time(), 0
         while time.time() - t0 < 2.0:

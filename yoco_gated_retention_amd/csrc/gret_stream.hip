@@ -13,7 +13,8 @@
 //
 // The segmented form mirrors the prefill's own memory pattern: each of G
 // workgroups (8 wavefronts, one per compute unit) streams its own contiguous
-// 1/G of the arrays, the loads go from HBM straight into LDS with
+// 1/G of the arrays (segments assigned to workgroups as the prefill assigns
+// them: one contiguous run of segments per XCD), the loads go from HBM straight into LDS with
 // buffer_load ... lds, D 1 KB blocks per stream and wavefront in flight, and
 // the output leaves from LDS through the registers with 16-byte stores.
 #include <hip/hip_runtime.h>
@@ -122,8 +123,12 @@ __global__ __launch_bounds__(512) void seg_stream_kernel(const char* a, const ch
                                                          const char* c, char* o, int64_t nblk) {
     constexpr int kSlots = D < 4 ? 4 : D;
     __shared__ __attribute__((aligned(16))) char lds[8 * kSlots * 3072];
-    const int64_t lo = static_cast<int64_t>(blockIdx.x) * nblk / gridDim.x;
-    const int64_t hi = static_cast<int64_t>(blockIdx.x + 1) * nblk / gridDim.x;
+    // segment of this workgroup in the prefill's order: the ids that land on
+    // one XCD (id mod 8) take one contiguous run of segments
+    const int64_t G = gridDim.x, x = blockIdx.x % 8, per = G / 8, rem = G % 8;
+    const int64_t seg = x * per + (x < rem ? x : rem) + blockIdx.x / 8;
+    const int64_t lo = seg * nblk / G;
+    const int64_t hi = (seg + 1) * nblk / G;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     char* mine = lds + w * D * 3072;
     const int64_t nit = (hi - lo + 7) / 8;
