@@ -116,10 +116,16 @@ int gret_prefill_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, in
  *   state_out           fp32 [B,H,dk,dv] or NULL; may be identical to state_in
  *                       (in place); any other overlap is GRET_ERR_ALIAS
  *   B, H, N             >= 1; N need not be a multiple of chunk (the tail chunk
- *                       is masked and state_out is exactly S_{N-1}); with
- *                       dtype BF16, N <= 2^23 (one head's rows are addressed
- *                       with 32-bit offsets), else GRET_ERR_SHAPE;
- *                       B*H <= 2^27 - 1 (also for the decode step)
+ *                       is masked and state_out is exactly S_{N-1});
+ *                       B*H <= 2^27 - 1 (also for the decode step). With dtype
+ *                       BF16 the head's length is not limited as such: each
+ *                       workgroup addresses the rows of its own piece of a
+ *                       head with 32-bit offsets, so ceil(B*H*ceil(N/chunk) /
+ *                       G) + 2 chunks (G = the launch's workgroups, one per
+ *                       compute unit, at most 1024) must fit 2^31 bytes of
+ *                       rows of max(dk, dv) bf16 -- about B*H*N <= 2^31 on a
+ *                       256-CU device -- else GRET_ERR_SHAPE (checked after
+ *                       the device's CU count is read, before any launch)
  *   dk, dv              64 or 128
  *   chunk               64, 128 or 256 -- the chunk length of the chunkwise form
  *   dtype               gret_dtype_t of q, k, v, out

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import oracle_output_gate_f64
 from tests.gpu_util import as_f64, eps, stats_eps, to_dev, to_host
 from workloads import CONFIGS, make_decode_inputs, make_prefill_inputs, slow_decay_log_gamma
 
@@ -315,6 +316,75 @@ def test_prefill_512k_slow_decay_all_heads(gret):
     cfg = CONFIGS["prefill_512k"]
     lg = slow_decay_log_gamma(cfg["B"], cfg["H"], cfg["N"])
     _full_check(gret, "prefill_512k", 64, log_gamma=lg)
+
+
+# ------------------------------------------- one head longer than 2^23 rows
+
+@pytest.mark.timeout(900)
+def test_prefill_head_longer_than_2_pow_23(gret):
+    """One head of 2^23 + 2^21 + 37 rows (past any 32-bit byte offset of the
+    head's own rows): the plain prefill at chunk 64 and 256 and the gated
+    prefill, inputs drawn on the device by a seeded generator (log-gates by the
+    workloads' gate map). The first 4096 rows are checked against the oracle
+    over the whole prefix. Sampled rows after that (around 2^23, at segment
+    starts, the last rows and 160 random ones) and the final state are checked
+    against the oracle over the 2048 rows ending at each, from a zero state:
+    the state carried into such a window reaches its last row only through
+    exp(sum of the window's later log-gates), which the test checks is below
+    exp(-60), far under the bf16 tolerance."""
+    from workloads import gate_log_gamma
+
+    N, d, W = (1 << 23) + (1 << 21) + 37, 128, 2048
+    say("prefill one head N=%d d=%d" % (N, d))
+    g = torch.Generator(device="cuda").manual_seed(2323)
+    qd = (torch.randn((1, 1, N, d), generator=g, device="cuda") * d ** -0.5).to(torch.bfloat16)
+    kd = (torch.randn((1, 1, N, d), generator=g, device="cuda") * d ** -0.5).to(torch.bfloat16)
+    vd = torch.randn((1, 1, N, d), generator=g, device="cuda").to(torch.bfloat16)
+    lg = gate_log_gamma(torch.randn((N,), generator=g, device="cuda").cpu().numpy())
+    lgd = torch.from_numpy(lg).cuda().view(1, 1, N)
+    gate = (2.0 * torch.randn((1, 1, N, d), generator=g, device="cuda")).to(torch.bfloat16)
+
+    # rows to check: window ends (a segment of the launch starts at chunk
+    # g * nc // 256 of the head on a 256-CU GPU)
+    rng = np.random.default_rng(23)
+    nc = (N + 63) // 64
+    starts = [(gg * nc // 256) * 64 for gg in (1, 2, 100, 200, 255)]
+    ends = np.unique(np.concatenate([
+        [4096, (1 << 23) - 1, 1 << 23, (1 << 23) + 1, N - 2, N - 1],
+        [r for p in starts for r in (p - 1, p, p + 1)],
+        rng.integers(4096, N, 160)]))
+    win = ends[:, None] - (W - 1) + np.arange(W)[None, :]   # [samples, W] rows
+    rows = np.unique(win.ravel())
+    at = np.searchsorted(rows, win)
+    ti = torch.from_numpy(rows).cuda()
+    hq, hk, hv = (to_host(t[0, 0, ti].contiguous()) for t in (qd, kd, vd))
+    wq, wk, wv = (np.ascontiguousarray(a[at])[None] for a in (hq, hk, hv))
+    wl = np.ascontiguousarray(lg[win])[None]
+    decay = wl[0, :, 1:].astype(np.float64).sum(axis=1)
+    assert decay.max() < -60.0, decay.max()
+    o_w, s_w, _ = oracle.oracle_prefill_f64(wq, wk, wv, wl)   # one window per oracle head
+    o_ref, s_ref = o_w[0, :, -1], s_w[0, -1]                  # the last window ends at N - 1
+    o0, _, _ = oracle.oracle_prefill_f64(
+        to_host(qd[:, :, :4096].contiguous()), to_host(kd[:, :, :4096].contiguous()),
+        to_host(vd[:, :, :4096].contiguous()), lg[None, None, :4096].copy())
+    eti = torch.from_numpy(ends).cuda()
+    y_ref = oracle_output_gate_f64(o_ref[None, None], to_host(gate[0, 0, eti].contiguous())[None, None])
+    y0 = oracle_output_gate_f64(o0, to_host(gate[:, :, :4096].contiguous()))
+    for chunk, gated in ((64, False), (256, False), (64, True)):
+        if gated:
+            out, st = gret.gret_prefill_gated(qd, kd, vd, lgd, gate, chunk=chunk)
+        else:
+            out, st = gret.gret_prefill(qd, kd, vd, lgd, None, chunk=chunk)
+        torch.cuda.synchronize()
+        e_o = eps(to_host(out[0, 0, eti].contiguous())[None, None], y_ref if gated else o_ref[None, None])
+        e_0 = eps(to_host(out[:, :, :4096].contiguous()), y0 if gated else o0)
+        e_s = eps(to_host(st)[0, 0], s_ref)
+        say("   chunk %d%s: %d sampled rows eps=%.3e, first 4096 rows eps=%.3e, state eps=%.3e"
+            % (chunk, " gated" if gated else "", len(ends), e_o, e_0, e_s))
+        assert e_o <= TOL_BF16 and e_0 <= TOL_BF16 and e_s <= TOL_BF16, (chunk, gated, e_o, e_0, e_s)
+        del out, st
+    del qd, kd, vd, gate, lgd
+    torch.cuda.empty_cache()
 
 
 # ------------------------------------------------------------------ decode

@@ -74,6 +74,12 @@ def _log_gamma(u: np.ndarray) -> np.ndarray:
     return (-np.logaddexp(0.0, -u.astype(np.float64)) / 16.0).astype(np.float32)
 
 
+def gate_log_gamma(u: np.ndarray) -> np.ndarray:
+    """The workloads' log-gates from gate logits u drawn elsewhere (for
+    inputs drawn on the device): float32(-softplus(-u) / 16)."""
+    return _log_gamma(np.asarray(u))
+
+
 def _draw_token_block(rng, n, dk, dv, dtype):
     u = rng.standard_normal(n, dtype=np.float32)
     q = rng.standard_normal((n, dk), dtype=np.float32)

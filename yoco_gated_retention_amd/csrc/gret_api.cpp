@@ -45,8 +45,6 @@ void* scratch_on(int dev) {
 }
 
 constexpr int64_t kMaxElems = int64_t(1) << 50;  // guards size arithmetic
-// The bf16 prefill addresses one head's rows through 32-bit buffer offsets.
-constexpr int64_t kMaxBf16PrefillN = int64_t(1) << 23;
 
 struct Span {
     uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -153,7 +151,6 @@ int prefill_impl(const void* q, const void* k, const void* v, const float* log_g
     int st = check_common(B, H, N, dk, dv, dtype);
     if (st != GRET_OK) return st;
     if (chunk != 64 && chunk != 128 && chunk != 256) return GRET_ERR_UNSUPPORTED;
-    if (dtype == GRET_DTYPE_BF16 && N > kMaxBf16PrefillN) return GRET_ERR_SHAPE;
     for (const void* p : {q, k, v, (const void*)out, (const void*)state_in, (const void*)state_out})
         if (p && !aligned(p, 16)) return GRET_ERR_UNSUPPORTED;
     if (!aligned(log_gamma, 4)) return GRET_ERR_UNSUPPORTED;
@@ -235,6 +232,11 @@ int prefill_impl(const void* q, const void* k, const void* v, const float* log_g
     int64_t G = static_cast<int64_t>(cus) * per_cu;
     if (G > gret::kMaxPrefillGroups) G = gret::kMaxPrefillGroups;
     const SegPlan plan = make_plan(B, H, N, chunk, G);
+    // a pass spans at most one workgroup's range of chunks (never more than a
+    // head), and issues loads up to two chunks past its end
+    const int64_t piece = (plan.T + plan.G - 1) / plan.G < plan.nc ? (plan.T + plan.G - 1) / plan.G
+                                                                  : plan.nc;
+    if ((piece + 2) * chunk > gret::prefill_pass_rows(dk, dv)) return GRET_ERR_SHAPE;
     if (use_scratch) {
         // the scratch holds the workspace of this device's plan (its number of
         // workgroups), not of the device-independent cap

@@ -21,6 +21,14 @@ constexpr float kLogGammaFloor = -80.0f;
 // its zero-state pass; its leading chunks are recomputed from S_in.
 constexpr float kSurvivalDropLog = -20.0f;
 
+// Rows of one head that a bf16 prefill pass (a segment, or the recomputed
+// leading chunks of one) may span: it addresses them through buffer ranges
+// with 32-bit byte offsets taken from its own first row, formed in 32-bit
+// arithmetic, so 2^31 bytes of the widest rows.
+constexpr int64_t prefill_pass_rows(int64_t dk, int64_t dv) {
+    return (int64_t(1) << 31) / (2 * (dk > dv ? dk : dv));
+}
+
 // Workgroups one launch may have (a single grid dimension). The C ABI checks
 // every launch of a call against it before anything is enqueued.
 constexpr int64_t kMaxGridGroups = 0x7fffffff;

@@ -355,13 +355,13 @@ __device__ float run_chunks(const Params& p, Smem<DK, DV, R>& sm, int64_t x, int
         *lead = full ? 0 : (ce - cb);
 #pragma unroll
         for (int tk = 0; tk < c::TK; ++tk) a.ds[tk] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const HeadRsrc hr = head_rsrc<DK, DV>(p, x);
+        // offsets are taken from this pass's first row (chunk cb)
+        const HeadRsrc hr = head_rsrc<DK, DV>(p, x, cb * c::C);
         TileRegs<DK, DV, R> tr;
-        load_tile<DK, DV, R>(hr, static_cast<uint32_t>(cb * c::C),
-                             static_cast<uint32_t>(cb * c::C), tr);
+        load_tile<DK, DV, R>(hr, 0, 0, tr);
         for (int64_t ch = cb; ch < ce; ++ch) {
-            const int64_t cpos = ch * c::C;
-            const int64_t nvalid = p.N - cpos < c::C ? p.N - cpos : c::C;
+            const int64_t cpos = (ch - cb) * c::C;
+            const int64_t nvalid = p.N - ch * c::C < c::C ? p.N - ch * c::C : c::C;
             const int rv = static_cast<int>((nvalid + kTile - 1) / kTile);
             for (int r = 0; r < rv; ++r) {
                 const uint32_t tpos = static_cast<uint32_t>(cpos + kTile * r);

@@ -711,19 +711,23 @@ template <int DK, int DV, bool GATED, bool ALL_FULL = false>
 __device__ float run_chunks(const Params& p, const Lds<DK, DV>& L, int64_t x, int64_t cb,
                            int64_t ce, bool full_from_start, Acc<DK, DV>& a, int64_t* lead) {
     float total = 0.0f;
-    const HeadRsrc hr = head_rsrc<DK, DV>(p, x);
+    // offsets are taken from this pass's first row (chunk cb)
+    const HeadRsrc hr = head_rsrc<DK, DV>(p, x, cb * kTile);
     // a zero-size range: stores through it are dropped, loads move no data
     const __amdgpu_buffer_rsrc_t drop = make_rsrc(p.out, 0);
     __amdgpu_buffer_rsrc_t gate_r = drop;
     const int nch = static_cast<int>(ce - cb);
     const bool all = ALL_FULL || full_from_start;
-    uint32_t pos = static_cast<uint32_t>(cb * kTile);
+    uint32_t pos = 0;
     // earlier passes of this workgroup: drain their memory operations, and let
     // every wavefront finish reading the buffers
     wait_vm<0>();
     lds_barrier();
     if constexpr (GATED) {
-        gate_r = make_rsrc(p.gate + x * p.N * DV, static_cast<uint32_t>(p.N * DV * 2));
+        const int64_t left = p.N - cb * kTile;
+        const int64_t rows = left < kRsrcRows<DK, DV> ? left : kRsrcRows<DK, DV>;
+        gate_r = make_rsrc(p.gate + (x * p.N + cb * kTile) * DV,
+                           static_cast<uint32_t>(rows * DV * 2));
         // the head's norm affine, read by every flush of the pass (after the
         // barrier of the first chunk)
         const int64_t h = x % p.H;
@@ -759,7 +763,7 @@ __device__ float run_chunks(const Params& p, const Lds<DK, DV>& L, int64_t x, in
     // (and, GATED, this wavefront's gate rows must have landed)
     if constexpr (GATED) wait_vm<0>();
     lds_barrier();
-    const uint32_t last_pos = static_cast<uint32_t>((ce - 1) * kTile);
+    const uint32_t last_pos = static_cast<uint32_t>((ce - 1 - cb) * kTile);
     const bf16_t* last_v = last == 0 ? L.v[0] : last == 1 ? L.v[1] : L.v[2];
     if constexpr (GATED)
         flush_tile_gated<DK, DV>(last_v, L.gt, L.aff, prev, last_pos, p.eps);

@@ -81,14 +81,24 @@ struct HeadRsrc {
 };
 
 template <int DK, int DV>
-__device__ inline HeadRsrc head_rsrc(const Params& p, int64_t x) {
+constexpr int64_t kRsrcRows = prefill_pass_rows(DK, DV);
+
+// Buffer ranges over the rows of head x from row0 on (to the head's end, at
+// most kRsrcRows rows): a pass addresses its rows relative to its own first
+// row, so no limit applies to the head's length, only to one pass's span.
+// Rows past the range read as zero and stores there are dropped.
+template <int DK, int DV>
+__device__ inline HeadRsrc head_rsrc(const Params& p, int64_t x, int64_t row0) {
     const int64_t N = p.N;
+    const int64_t left = N - row0;
+    const int64_t rows = left < kRsrcRows<DK, DV> ? left : kRsrcRows<DK, DV>;
+    const int64_t r0 = x * N + row0;
     HeadRsrc hr;
-    hr.q = make_rsrc(p.q + x * N * DK, static_cast<uint32_t>(N * DK * 2));
-    hr.k = make_rsrc(p.k + x * N * DK, static_cast<uint32_t>(N * DK * 2));
-    hr.v = make_rsrc(p.v + x * N * DV, static_cast<uint32_t>(N * DV * 2));
-    hr.lg = make_rsrc(p.log_gamma + x * N, static_cast<uint32_t>(N * 4));
-    hr.out = make_rsrc(p.out + x * N * DV, static_cast<uint32_t>(N * DV * 2));
+    hr.q = make_rsrc(p.q + r0 * DK, static_cast<uint32_t>(rows * DK * 2));
+    hr.k = make_rsrc(p.k + r0 * DK, static_cast<uint32_t>(rows * DK * 2));
+    hr.v = make_rsrc(p.v + r0 * DV, static_cast<uint32_t>(rows * DV * 2));
+    hr.lg = make_rsrc(p.log_gamma + r0, static_cast<uint32_t>(rows * 4));
+    hr.out = make_rsrc(p.out + r0 * DV, static_cast<uint32_t>(rows * DV * 2));
     return hr;
 }
 
