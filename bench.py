@@ -741,8 +741,9 @@ def bench_swa(gret, dev, B=1, H=24, N=524288, d=128, W=1024, Bd=256, reps=10, se
     achieved = nbytes / (us * 1e-6) / 1e9
     res["decode"] = {"workload": "swa_decode_b%d_h%d_d%d_w%d" % (Bd, H, d, W),
                      "us_per_step": us, "steps_per_s": 1e6 / us,
-                     "roofline": {"kernel": "swa_append_kernel + xattn_split_kernel + "
-                                            "xattn_combine_kernel", "bound": "hbm",
+                     "roofline": {"kernel": "swa_append_kernel + xattn_split_kernel (one range "
+                                            "per ring here, so no xattn_combine_kernel launch)",
+                                  "bound": "hbm",
                                   "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                                   "algorithmic_bytes_per_launch": nbytes}}

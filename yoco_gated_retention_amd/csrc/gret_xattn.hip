@@ -24,7 +24,10 @@
 //     leaves the registers.
 // The wavefronts merge through LDS, the workgroup writes its partial (max,
 // sum, unnormalised output) per head, and a second kernel merges the ranges
-// with log-sum-exp weights.
+// with log-sum-exp weights. When the plan has one range per (sequence, KV
+// head) -- many short caches, such as the sliding-window rings -- the
+// workgroup writes the normalised output itself and the second launch is
+// skipped.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -262,8 +265,14 @@ __global__ __launch_bounds__(kXThreads) void xattn_split_kernel(XParams p) {
             lsum += f * s_ml[ww][h][1];
             a += f * reinterpret_cast<const float*>(k0_ + ww * c::TILE)[h * D + j];
         }
-        pacc[e] = a;
-        if (j == 0) ml[h] = make_float2(M, lsum);
+        if (p.S == 1) {
+            // one range per (sequence, KV head): this is the whole softmax, and
+            // the output is what the merge of a single range would give
+            p.out[(b * p.Hq + head0 + h) * D + j] = to_bf16(a / lsum);
+        } else {
+            pacc[e] = a;
+            if (j == 0) ml[h] = make_float2(M, lsum);
+        }
     }
 }
 
@@ -351,7 +360,7 @@ hipError_t launch_d(const XAttnArgs& a) {
     hipLaunchKernelGGL((xattn_split_kernel<D>), dim3(static_cast<unsigned>(a.B * a.Hkv * plan.S)),
                        dim3(kXThreads), 0, a.stream, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || plan.S == 1) return e;  // one range: the split kernel wrote out
     hipLaunchKernelGGL((xattn_combine_kernel<D>), dim3(static_cast<unsigned>(a.B * a.Hq)),
                        dim3(kXCombineThreads), 0, a.stream, p);
     return hipGetLastError();
