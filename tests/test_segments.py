@@ -6,7 +6,9 @@ visits and the slot it writes, and the count the combine kernel reads. They are
 checked here by brute force: slots are unique, in range (below the per-head
 bound that sizes the workspace), in sequence order, and every (head, chunk)
 pair is covered exactly once. The map from a workgroup's launch index to its
-segment (contiguous segment runs per XCD) must be a bijection.
+segment (contiguous segment runs per XCD) must be a bijection, and the bound
+on a piece's length that the prefill checks its 32-bit row offsets against must
+hold for every piece.
 """
 import os
 import subprocess
@@ -27,7 +29,8 @@ int main(int argc, char** argv) {
     p.BH = atoll(argv[1]); p.nc = atoll(argv[2]); p.T = p.BH * p.nc;
     long long G = atoll(argv[3]); p.G = G < p.T ? G : p.T;
     p.max_seg = seg_max_per_head(p.BH, p.nc, p.G);
-    printf("P %lld %lld\n", (long long)p.G, (long long)p.max_seg);
+    printf("P %lld %lld %lld\n", (long long)p.G, (long long)p.max_seg,
+           (long long)seg_max_piece_chunks(p));
     for (int64_t g = 0; g < p.G; ++g) {
         int64_t t = seg_lo(p, g), hi = seg_lo(p, g + 1);
         while (t < hi) {
@@ -67,7 +70,7 @@ CASES = [(1, 1, 1), (1, 1, 512), (2, 8, 3), (24, 8192, 256), (24, 2048, 1024), (
 def test_segments_cover_and_slots(driver, BH, nc, G):
     out = subprocess.run([driver, str(BH), str(nc), str(G)], check=True, capture_output=True,
                          text=True).stdout.split("\n")
-    Geff, max_seg = map(int, out[0].split()[1:])
+    Geff, max_seg, max_piece = map(int, out[0].split()[1:])
     assert Geff == min(G, BH * nc)
     covered = {}
     slots = {}
@@ -78,6 +81,8 @@ def test_segments_cover_and_slots(driver, BH, nc, G):
             g, x, cb, ce, slot = map(int, line.split()[1:])
             assert 0 <= x < BH and 0 <= cb < ce <= nc
             assert 0 <= slot < max_seg
+            # the bound the prefill's 32-bit row offsets are checked against
+            assert ce - cb <= max_piece
             assert (x, slot) not in slots, "slot written twice"
             slots[(x, slot)] = (cb, ce)
             for c in range(cb, ce):
@@ -90,6 +95,9 @@ def test_segments_cover_and_slots(driver, BH, nc, G):
             b, g = map(int, line.split()[1:])
             seg_of[b] = g
     assert len(covered) == BH * nc
+    # ... and it is attained by some piece (or exceeds the longest by one)
+    longest = max(ce - cb for cb, ce in slots.values())
+    assert longest <= max_piece <= longest + 1
     # the launch-index -> segment map is a bijection of [0, G), and the ids
     # that share an XCD (b mod 8) take one contiguous run of segments in order
     assert sorted(seg_of) == list(range(Geff)) and sorted(seg_of.values()) == list(range(Geff))

@@ -232,11 +232,9 @@ int prefill_impl(const void* q, const void* k, const void* v, const float* log_g
     int64_t G = static_cast<int64_t>(cus) * per_cu;
     if (G > gret::kMaxPrefillGroups) G = gret::kMaxPrefillGroups;
     const SegPlan plan = make_plan(B, H, N, chunk, G);
-    // a pass spans at most one workgroup's range of chunks (never more than a
-    // head), and issues loads up to two chunks past its end
-    const int64_t piece = (plan.T + plan.G - 1) / plan.G < plan.nc ? (plan.T + plan.G - 1) / plan.G
-                                                                  : plan.nc;
-    if ((piece + 2) * chunk > gret::prefill_pass_rows(dk, dv)) return GRET_ERR_SHAPE;
+    // a pass issues loads up to two chunks past its last one
+    if ((gret::seg_max_piece_chunks(plan) + 2) * chunk > gret::prefill_pass_rows(dk, dv))
+        return GRET_ERR_SHAPE;
     if (use_scratch) {
         // the scratch holds the workspace of this device's plan (its number of
         // workgroups), not of the device-independent cap

@@ -59,6 +59,15 @@ GRET_HD int64_t seg_count(const SegPlan& p, int64_t x) {
     return 1 + (b > a ? b - a : 0);
 }
 
+// Longest piece, in chunks: a workgroup's range has at most ceil(T / G)
+// chunks, and a piece is that range cut at head boundaries (at most nc).
+// A prefill pass (a segment, or the recomputed leading chunks of one) spans
+// at most this many chunks.
+GRET_HD int64_t seg_max_piece_chunks(const SegPlan& p) {
+    const int64_t r = (p.T + p.G - 1) / p.G;
+    return r < p.nc ? r : p.nc;
+}
+
 // Segment of the workgroup with launch index b. The hardware hands workgroup
 // ids to the chip's XCDs round-robin (id mod kXcds), and each XCD has its own
 // L2 and address-translation caches. So that XCD x works on one contiguous
