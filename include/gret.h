@@ -312,7 +312,10 @@ int gret_head_projection(const void* x, const void* w_key, const void* w_gamma, 
  *   k_ring, v_ring  [B,Hkv,window,d] bf16, or both NULL: when given, slot
  *                p mod window receives position p for the last min(N, window)
  *                positions (other slots are left as they are)
- *   N, window    1 .. 2^23;  d 64 or 128;  Hq a multiple of Hkv;  B*Hq*max(N,
+ *   N            >= 1 (each workgroup addresses its query tile and its window
+ *                of keys from their own first rows, so the prompt's length
+ *                is limited only by the sizes below)
+ *   window       1 .. 2^23;  d 64 or 128;  Hq a multiple of Hkv;  B*Hq*max(N,
  *                window)*d <= 2^50 and each launch <= 2^31 - 1 workgroups
  *                (B*Hq*ceil(N/256) for the attention)
  *   scale        finite (usually d^-1/2), else GRET_ERR_VALUE

@@ -245,7 +245,7 @@ def test_swa_validation(lib):
     assert swa_pre(lib, rk=None) == NULL              # one ring without the other
     assert swa_pre(lib, N=0) == SHAPE
     assert swa_pre(lib, window=0) == SHAPE
-    assert swa_pre(lib, N=(1 << 23) + 1) == SHAPE
+    assert swa_pre(lib, window=(1 << 23) + 1) == SHAPE
     assert swa_pre(lib, d=96) == UNSUP
     assert swa_pre(lib, Hq=25) == UNSUP
     assert swa_pre(lib, dtype=F32) == UNSUP

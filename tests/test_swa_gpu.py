@@ -162,6 +162,51 @@ def test_swa_prefill_full_size_sampled(gret):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(600)
+def test_swa_prefill_longer_than_2_pow_23(gret):
+    """One head of 2^23 + 2^20 + 77 positions (past any 32-bit byte offset of
+    the head's rows), window 1024, with the rings: sampled rows (around 2^23,
+    at query-tile edges, the last rows and 200 random ones) against the oracle
+    over each row's window, and the rings against the prompt's last 1024
+    keys and values (slot p mod 1024 holds position p)."""
+    N, d, W = (1 << 23) + (1 << 20) + 77, 128, 1024
+    say("swa_prefill one head N=%d d=%d window=%d" % (N, d, W))
+    g = torch.Generator(device="cuda").manual_seed(2424)
+    q = torch.randn((1, 1, N, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((1, 1, N, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((1, 1, N, d), generator=g, device="cuda").to(torch.bfloat16)
+    rk = torch.zeros((1, 1, W, d), dtype=torch.bfloat16, device="cuda")
+    rv = torch.zeros_like(rk)
+    out = gret.gret_swa_prefill(q, k, v, W, k_ring=rk, v_ring=rv)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(24)
+    ends = np.unique(np.concatenate([
+        [0, 255, 256, W, (1 << 23) - 256, (1 << 23) - 1, 1 << 23, (1 << 23) + 1, N - 2, N - 1],
+        rng.integers(0, N, 200)]))
+    lo = np.maximum(ends - (W - 1), 0)
+    need = np.unique(np.concatenate([np.arange(a, b + 1) for a, b in zip(lo, ends)]))
+    ti = torch.from_numpy(need).cuda()
+    # a compact prompt holding just the needed rows; row r of it is position need[r]
+    hq, hk, hv = (to_host(t[0, 0, ti].contiguous()) for t in (q, k, v))
+    worst = 0.0
+    for e, a in zip(ends, lo):
+        r0, r1 = np.searchsorted(need, [a, e])
+        # rows a..e are contiguous in `need`: a prompt of e - a + 1 rows whose
+        # last row is position e (its window starts at a)
+        qq = np.zeros((1, 1, r1 - r0 + 1, d), np.uint16)
+        qq[0, 0, -1] = hq[r1]
+        ref = oracle_swa_prefill_f64(qq, hk[None, None, r0:r1 + 1], hv[None, None, r0:r1 + 1], W,
+                                     rows=[r1 - r0])[0, 0, 0]
+        got = to_host(out[0, 0, int(e)].contiguous())
+        worst = max(worst, eps(got, ref))
+    say("   %d sampled rows: worst eps_out=%.3e" % (len(ends), worst))
+    assert worst <= TOL
+    slots = torch.arange(N - W, N, device="cuda") % W
+    assert torch.equal(rk[0, 0, slots], k[0, 0, N - W:]) and torch.equal(rv[0, 0, slots], v[0, 0, N - W:])
+    del q, k, v, out, rk, rv
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("q_scale", [8.0, 30.0])
 def test_swa_prefill_peaked_scores(gret, q_scale):
     """Scores with standard deviation 8 and 30: the running softmax maximum

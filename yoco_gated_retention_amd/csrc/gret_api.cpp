@@ -534,7 +534,7 @@ int gret_swa_prefill(const void* q, const void* k, const void* v, void* out, voi
     if ((k_ring == nullptr) != (v_ring == nullptr)) return GRET_ERR_NULL;
     int st = check_swa(B, Hq, Hkv, d, window, dtype);
     if (st != GRET_OK) return st;
-    if (N < 1 || N > kSwaMaxN) return GRET_ERR_SHAPE;
+    if (N < 1) return GRET_ERR_SHAPE;
     const int64_t span_rows = N > window ? N : window;  // positions of q/k/v/out, of the rings
     if (B * Hq > kMaxElems / (span_rows * d)) return GRET_ERR_SHAPE;
     if (gret::swa_prefill_groups(B, Hq, Hkv, N, d, window, k_ring != nullptr) >

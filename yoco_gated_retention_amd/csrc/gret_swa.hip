@@ -248,8 +248,9 @@ __device__ inline void swa_step(int t, int n, int64_t kb0, __amdgpu_buffer_rsrc_
                                 int64_t qi, int64_t qw0, int64_t W, float cl, SwaAcc<D>& st) {
     wait_vm<0>();
     lds_barrier();
+    // kr and vr start at key block kb0
     dma_stage<D>(kr, vr, swa_kst<X ^ 1>(), swa_vst<X ^ 1>(),
-                 static_cast<uint32_t>((kb0 + kSBlocks * (t + 1)) * kSK));
+                 static_cast<uint32_t>(kSBlocks * (t + 1) * kSK));
 #pragma unroll
     for (int hb = 0; hb < kSBlocks; ++hb) {
         const int i = kSBlocks * t + hb;
@@ -282,22 +283,29 @@ __global__ __launch_bounds__(kSThreads) void swa_prefill_kernel(SwaParams p) {
     const int li = lane & 31, hh = lane >> 5;
     const int64_t q0 = qt * kSQ, qw0 = q0 + 32 * w, qi = qw0 + li;
 
+    // Buffer ranges start at this tile's first query and its first key block
+    // (32-bit offsets: a range spans at most 2^31 bytes, and a tile addresses
+    // fewer than W + 512 rows of it), so the prompt's length is not limited.
+    constexpr int64_t kRows = (int64_t(1) << 31) / (2 * D);
+    const int64_t q_rows = N - q0 < kRows ? N - q0 : kRows;
     const __amdgpu_buffer_rsrc_t qr =
-        make_rsrc(p.q + bh * N * D, static_cast<uint32_t>(N * D * 2));
+        make_rsrc(p.q + (bh * N + q0) * D, static_cast<uint32_t>(q_rows * D * 2));
     bf16x8 qf[c::KS];
 #pragma unroll
     for (int ks = 0; ks < c::KS; ++ks)
         qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                qr, static_cast<uint32_t>((qi * D + 16 * ks + 8 * hh) * 2),
+                                                qr, static_cast<uint32_t>(((qi - q0) * D + 16 * ks + 8 * hh) * 2),
                                                 0, 0));
     const int64_t kvh = b * p.Hkv + g;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k + kvh * N * D, static_cast<uint32_t>(N * D * 2));
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.v + kvh * N * D, static_cast<uint32_t>(N * D * 2));
-
     const int64_t jlo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
     const int64_t jhi = q0 + kSQ < N ? q0 + kSQ : N;
     const int64_t kb0 = jlo / kSK, kb1 = (jhi + kSK - 1) / kSK;
     const int n = static_cast<int>(kb1 - kb0);
+    const int64_t k_rows = N - kb0 * kSK < kRows ? N - kb0 * kSK : kRows;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k + (kvh * N + kb0 * kSK) * D,
+                                                static_cast<uint32_t>(k_rows * D * 2));
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.v + (kvh * N + kb0 * kSK) * D,
+                                                static_cast<uint32_t>(k_rows * D * 2));
 
     SwaAcc<D> st;
 #pragma unroll
@@ -308,7 +316,7 @@ __global__ __launch_bounds__(kSThreads) void swa_prefill_kernel(SwaParams p) {
     st.l = 0.0f;
     const float cl = p.scale_log2;
 
-    dma_stage<D>(kr, vr, swa_kst<0>(), swa_vst<0>(), static_cast<uint32_t>(kb0 * kSK));
+    dma_stage<D>(kr, vr, swa_kst<0>(), swa_vst<0>(), 0);
     const int stages = (n + kSBlocks - 1) / kSBlocks;
     int t = 0;
     for (; t + 2 <= stages; t += 2) {
