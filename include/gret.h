@@ -249,8 +249,12 @@ int gret_decode_step_gated(const void* q, const void* k, const void* v, const fl
  *              accesses stay inside the caches)
  *   scale      finite (usually d^-1/2), else GRET_ERR_VALUE
  *   dtype      GRET_DTYPE_BF16 only (else GRET_ERR_UNSUPPORTED)
- *   d          64 or 128;  Hq a multiple of Hkv with Hq / Hkv <= 16;  L <= 2^23;
- *              B*Hq <= 2^30 - 1
+ *   d          64 or 128;  Hq a multiple of Hkv with Hq / Hkv <= 16;
+ *              B*Hq <= 2^30 - 1;  B*Hkv*L*128 <= 2^50;  L needs no other
+ *              bound until the plan would need more than 1024 ranges per
+ *              sequence and KV head (L above about 2^33 at d = 128): each
+ *              range addresses its positions with 32-bit offsets from its
+ *              own first position
  *   workspace  at least gret_cross_attention_workspace_bytes(...) bytes,
  *              256-byte aligned (per-range partial results); calls that share
  *              a workspace must be ordered on one stream

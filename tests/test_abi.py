@@ -187,7 +187,10 @@ def test_cross_attention_validation(lib):
     assert lib.gret_cross_attention_workspace_bytes(2, 24, 8, 4096, 128, None) == NULL
     assert xattn(lib, q=None) == NULL
     assert xattn(lib, L=0) == SHAPE
-    assert xattn(lib, L=(1 << 23) + 1) == SHAPE
+    assert xattn(lib, B=1, Hq=1, Hkv=1, L=1 << 34) == SHAPE  # more ranges than the merge takes
+    # caches longer than 2^23 positions are split into ranges that fit 32-bit offsets
+    assert lib.gret_cross_attention_workspace_bytes(1, 8, 8, (1 << 24) + 5, 128,
+                                                    ctypes.byref(n)) == OK
     assert xattn(lib, d=96) == UNSUP
     assert xattn(lib, Hq=25) == UNSUP                 # not a multiple of Hkv
     assert xattn(lib, Hq=136) == UNSUP                # 17 query heads per KV head

@@ -115,3 +115,29 @@ def test_512k_context_all_heads(gret):
 def test_batch_of_32k_contexts(gret):
     check(gret, 16, 24, 8, 32768, 128, lengths=[32768 - 97 * i for i in range(16)], seed=12,
           label="16x32k")
+
+
+@pytest.mark.timeout(900)
+def test_cache_longer_than_2_pow_23(gret):
+    """One sequence whose cache holds 2^23 + 2^20 + 33 positions (past any
+    32-bit byte offset of the cache's rows; every range addresses its
+    positions from its own first one), 8 query heads on one KV head, inputs
+    drawn on the device by a seeded generator; all positions, then a
+    shorter valid length."""
+    B, Hq, Hkv, L, d = 1, 8, 1, (1 << 23) + (1 << 20) + 33, 128
+    say("xattn long cache B=%d Hq=%d Hkv=%d L=%d d=%d" % (B, Hq, Hkv, L, d))
+    g = torch.Generator(device="cuda").manual_seed(2525)
+    q = torch.randn((B, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((B, Hkv, L, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, Hkv, L, d), generator=g, device="cuda").to(torch.bfloat16)
+    hq, hk, hv = to_host(q), to_host(k), to_host(v)
+    for lengths in (None, [L - 12345]):
+        lens_dev = None if lengths is None else torch.tensor(lengths, dtype=torch.int32,
+                                                             device="cuda")
+        out = gret.gret_cross_attention_decode(q, k, v, lens_dev, None)
+        torch.cuda.synchronize()
+        e = eps(to_host(out), oracle_cross_attention_f64(hq, hk, hv, lengths, None))
+        say("   lengths=%s eps=%.3e" % (lengths, e))
+        assert e <= TOL, e
+    del q, k, v
+    torch.cuda.empty_cache()

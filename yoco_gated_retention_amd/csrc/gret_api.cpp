@@ -401,13 +401,18 @@ namespace {
 
 int check_xattn(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d) {
     if (B < 1 || Hq < 1 || Hkv < 1 || L < 1) return GRET_ERR_SHAPE;
-    if (B > kMaxElems || Hq > kMaxElems / B || L > (int64_t(1) << 23)) return GRET_ERR_SHAPE;
+    if (B > kMaxElems || Hq > kMaxElems / B) return GRET_ERR_SHAPE;
     if (B * Hkv > kMaxElems / L / 128 || B * Hq > kMaxElems / 128) return GRET_ERR_SHAPE;
-    // the combine launch has B*Hq workgroups, the split launch at most
-    // B*Hkv + 1023 (about 1024 in all, or one per sequence and KV head)
+    // the combine launch has B*Hq workgroups, the split launch B*Hkv*S (S
+    // ranges per sequence and KV head: about 1024 workgroups in all, or one
+    // per sequence and KV head, or as many as a very long cache needs)
     if (B * Hq > gret::kMaxGridGroups / 2) return GRET_ERR_SHAPE;
     if (d != 64 && d != 128) return GRET_ERR_UNSUPPORTED;
     if (Hq % Hkv != 0 || Hq / Hkv > 16) return GRET_ERR_UNSUPPORTED;
+    // the combine merges at most kXAttnTargetGroups ranges per head
+    const gret::XAttnPlan plan = gret::xattn_plan(B, Hq, Hkv, L, d);
+    if (plan.S > gret::kXAttnTargetGroups || B * Hkv * plan.S > gret::kMaxGridGroups)
+        return GRET_ERR_SHAPE;
     return GRET_OK;
 }
 

@@ -111,6 +111,10 @@ struct XAttnArgs {
 // Position ranges per (sequence, KV head) and the workspace they need; the plan
 // depends only on the shapes (not on the device).
 constexpr int64_t kXAttnTargetGroups = 1024;
+// Cached positions one range of the cross-attention plan may span (with the
+// tile a wavefront loads past its end): its buffer ranges take 32-bit byte
+// offsets from the range's first position, 2^31 bytes of rows of d bf16.
+constexpr int64_t xattn_range_rows(int64_t d) { return (int64_t(1) << 31) / (2 * d); }
 struct XAttnPlan {
     int64_t S = 1, SL = 0;
     size_t acc_off = 0, bytes = 0;

@@ -39,6 +39,8 @@ namespace {
 
 constexpr int kXTile = 32;     // positions per tile
 constexpr int kXWaves = 4;     // wavefronts per workgroup
+template <int D>
+constexpr int64_t kXRangeRows = xattn_range_rows(D);
 constexpr int kXThreads = 64 * kXWaves;
 
 
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(kXThreads) void xattn_split_kernel(XParams p) {
         if (threadIdx.x < p.G) ml[threadIdx.x] = make_float2(-INFINITY, 0.0f);
         return;
     }
-    const uint32_t hi = static_cast<uint32_t>(hi64);
+    const uint32_t hi = static_cast<uint32_t>(hi64 - lo);
     const int64_t head0 = kvh * p.G;
     bf16x8 qf[c::KS];
 #pragma unroll
@@ -188,9 +190,13 @@ __global__ __launch_bounds__(kXThreads) void xattn_split_kernel(XParams p) {
         else
             qf[ks] = bf16x8{};
     }
-    const int64_t kv_base = bg * p.L * D;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k + kv_base, static_cast<uint32_t>(p.L * D * 2));
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.v + kv_base, static_cast<uint32_t>(p.L * D * 2));
+    // buffer ranges start at this range's first position (32-bit offsets: a
+    // range of the plan spans at most kXRangeRows rows), so positions below
+    // are relative to lo
+    const int64_t kv_base = (bg * p.L + lo) * D;
+    const int64_t rows = p.L - lo < kXRangeRows<D> ? p.L - lo : kXRangeRows<D>;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k + kv_base, static_cast<uint32_t>(rows * D * 2));
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.v + kv_base, static_cast<uint32_t>(rows * D * 2));
 
     float m_run = -INFINITY, l_run = 0.0f;
     f32x4 acc[c::VT];
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(kXThreads) void xattn_split_kernel(XParams p) {
         }
     };
     const uint32_t step = kXTile * kXWaves;
-    uint32_t pos = static_cast<uint32_t>(lo) + kXTile * w;
+    uint32_t pos = kXTile * w;
     if (pos < hi) issue(0, pos);
     // unrolled by two so that every access's buffer is a compile-time fact
     while (pos < hi) {
@@ -379,6 +385,11 @@ XAttnPlan xattn_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d) {
     if (S > max_s) S = max_s;
     if (S < 1) S = 1;
     const int64_t round = static_cast<int64_t>(kXTile) * kXWaves;
+    // a range (plus the tile a wavefront may load past it) must fit the 32-bit
+    // offsets of its buffer ranges
+    const int64_t max_sl = (xattn_range_rows(d) - round) / round * round;
+    const int64_t min_s = (L + max_sl - round - 1) / (max_sl - round);
+    if (S < min_s) S = min_s;
     int64_t SL = (L + S - 1) / S;
     SL = (SL + round - 1) / round * round;
     S = (L + SL - 1) / SL;
